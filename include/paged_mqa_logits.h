@@ -1,0 +1,143 @@
+/*
+ * paged_mqa_logits.h -- C ABI of the paged MQA-logits indexer library
+ * (libidx_paged_mqa.so, HIP kernels for gfx950).
+ *
+ * What is computed.  The DSA indexer scores one query row against every
+ * cached c4-position of that row's paged key cache.  The pages describe it as
+ * attention scores between the current query and all cached positions, with
+ * a ReLU, a per-head weighting and a position-specific scale ("The Dispatch
+ * Wire: Connecting a Triton Indexer Kernel to Production Inference",
+ * section "The Road to This Message"), the fallback's op chain being a batched
+ * QK product, ReLU, weight scaling and a sum over heads (same section).  With
+ * H = 64 heads, D = 128 and pages of 64 c4-positions:
+ *
+ *   L_b          = clamp(seqlens[b], 0, table_width * 64)
+ *   out[b][p]    = sum_h w[b][h] * ReLU( s_p * <q[b][h][:], k_p[:]> )   p <  L_b
+ *   out[b][p]    = -inf                                                 p >= L_b
+ *
+ * where position p = 64*j + i lives in physical page g = page_table_b[j] at
+ * slot i, k_p is its 128-value key and s_p its scale (1 for bf16 keys).
+ * ReLU propagates NaN.  Positions at or past the row's length are -inf
+ * ("The Final Gate: Validating a Custom Triton Indexer Kernel Before Production
+ * Deployment", section "What the Test Output Reveals").
+ *
+ * Launch model.  One fixed grid whose shape depends only on the scalar
+ * arguments; a work unit whose pages all start at or past L_b writes -inf and
+ * exits without reading the page table or the keys, so the cost follows the
+ * actual lengths while the grid and the output shape stay fixed and the call
+ * can be captured into a HIP graph ("The Moment the Context-Length Tax
+ * Vanished: Committing the O(actual) Triton Indexer", section "The Commit:
+ * Engineering as Narrative").  Pages are read through the page table on the
+ * fly; no gathered copy of the cache is ever made (the bf16 prefill failure in
+ * "The Dispatch Decision: Wiring a Triton Kernel into Production", section
+ * "The Problem That Led Here").
+ *
+ * Ownership and threading.  Every pointer argument is a DEVICE pointer owned by
+ * the caller.  The library holds no state, allocates no memory, never
+ * synchronises the host and enqueues its work on `stream` (NULL = the null
+ * stream).  Calls are thread-safe; calls that write the same `out` race.
+ *
+ * Errors.  Every entry point validates its arguments on the host and returns
+ * an idx_status; it never aborts, prints or throws.  Nothing is launched when
+ * the return value is not IDX_OK.  Device data is never inspected on the host:
+ *  - seqlens are clamped to [0, table_width*64] on the device;
+ *  - a page-table entry that is read (its page holds a live position) and lies
+ *    outside [0, num_pages) is never dereferenced: that page's live positions
+ *    are written as NaN (its masked positions still get -inf);
+ *  - page-table entries of slots past a row's live pages are never read and
+ *    may hold anything (e.g. -1 padding).
+ */
+#ifndef IDX_PAGED_MQA_LOGITS_H
+#define IDX_PAGED_MQA_LOGITS_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Version of this ABI; bumped on any incompatible change. */
+#define IDX_ABI_VERSION 1
+
+/* Fixed shape of the indexer: heads, head dimension, positions per page. */
+#define IDX_NUM_HEADS 64
+#define IDX_HEAD_DIM 128
+#define IDX_PAGE_POSITIONS 64
+
+typedef enum {
+  IDX_OK = 0,
+  IDX_ERR_NULL = -1,        /* a required pointer is NULL (or kscale given for bf16) */
+  IDX_ERR_UNSUPPORTED = -2, /* num_heads != 64 or head_dim != 128 */
+  IDX_ERR_SHAPE = -3,       /* negative or oversized dimension, stride too small */
+  IDX_ERR_ALIGN = -4,       /* pointer or stride misaligned */
+  IDX_ERR_LAUNCH = -5       /* the HIP launch reported an error */
+} idx_status;
+
+/*
+ * fp8-key variant.  Keys are OCP e4m3fn bytes with one fp32 scale per
+ * position; the cache block of the pages holds 64 positions x 128 e4m3 values
+ * followed by 64 fp32 scales, 8,448 bytes in all ("The Dispatch Wire ...",
+ * section "The Reasoning and Decision-Making"; "The Final Gate ...", section
+ * "Assumptions and Knowledge Required").
+ *
+ *   q          bf16 [rows][64][128], contiguous, 16-byte aligned.
+ *   kv_pages   key pool.  Page g starts at (const char*)kv_pages +
+ *              g*kv_page_stride and holds [64][128] e4m3fn bytes, position
+ *              major.  16-byte aligned.
+ *   kscale     scale of slot i of page g is the fp32 at
+ *              (const char*)kscale + g*kscale_page_stride + 4*i.  For the
+ *              fused block layout pass kv_pages + 8192 and a stride of 8448.
+ *              4-byte aligned.
+ *   page_table int32; row b's table is page_table + b*page_table_row_stride,
+ *              table_width entries of physical page ids.  A stride of 0 makes
+ *              every row share one table (the prefill case: T query tokens of
+ *              one request).  4-byte aligned.
+ *   seqlens    int32 [rows], valid c4-positions per row.  4-byte aligned.
+ *   weights    fp32 [rows][64] per-head weights, 16-byte aligned.
+ *   out        fp32 [rows][table_width*64], 16-byte aligned.  Every element is
+ *              written (finite, NaN for an invalid page id, or -inf).
+ *   rows, table_width       >= 0; 0 returns IDX_OK with no launch.
+ *                           table_width <= 16,777,216.
+ *   num_heads, head_dim     must be 64 and 128.
+ *   num_pages               pages in the pool (bound for page ids), >= 0.
+ *   kv_page_stride          bytes, >= 8192, multiple of 16.
+ *   kscale_page_stride      bytes, >= 256, multiple of 4.
+ *   page_table_row_stride   int32 elements, >= 0.
+ *   stream                  HIP stream the kernel is enqueued on.
+ */
+int idx_paged_mqa_logits_fp8(const void* q, const void* kv_pages, const float* kscale,
+                             const int32_t* page_table, const int32_t* seqlens,
+                             const float* weights, float* out, int32_t rows, int32_t num_heads,
+                             int32_t head_dim, int32_t table_width, int64_t num_pages,
+                             int64_t kv_page_stride, int64_t kscale_page_stride,
+                             int64_t page_table_row_stride, hipStream_t stream);
+
+/*
+ * bf16-key variant: keys stored as bf16, 256 bytes per position and no scale
+ * (s_p = 1), the layout of the bf16 indexer store in "The Dispatch Decision:
+ * Wiring a Triton Kernel into Production", section "The Problem That Led Here".
+ * Same arguments as the fp8 variant except:
+ *   kv_pages            page g holds [64][128] bf16; kv_page_stride >= 16384,
+ *                       multiple of 16.
+ *   kscale              must be NULL (else IDX_ERR_NULL); kscale_page_stride
+ *                       is ignored.
+ */
+int idx_paged_mqa_logits_bf16(const void* q, const void* kv_pages, const float* kscale,
+                              const int32_t* page_table, const int32_t* seqlens,
+                              const float* weights, float* out, int32_t rows, int32_t num_heads,
+                              int32_t head_dim, int32_t table_width, int64_t num_pages,
+                              int64_t kv_page_stride, int64_t kscale_page_stride,
+                              int64_t page_table_row_stride, hipStream_t stream);
+
+/* Static, human-readable text for an idx_status value (never NULL). */
+const char* idx_status_string(int status);
+
+/* IDX_ABI_VERSION of the loaded library. */
+int idx_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IDX_PAGED_MQA_LOGITS_H */

@@ -1,0 +1,166 @@
+/*
+ * oracle.c -- TEST INFRASTRUCTURE ONLY.  A plain, slow CPU definition of the
+ * paged MQA-logits indexer, used to check the HIP library.  Nothing in the
+ * library links, includes or calls this file; only the tests, the smoke check
+ * and the benchmark's CPU-baseline leg load it.
+ *
+ * Arithmetic is float64 throughout, in a fixed order: for each output the dot
+ * product runs over d = 0..127 ascending, then heads h = 0..63 ascending.
+ * Parallelism (OpenMP) is only over independent outputs, so it never changes
+ * any result.
+ *
+ * Sources (the pages' titles and sections):
+ *  - the computation: a per-head QK score, scaled per position, passed through
+ *    ReLU, weighted per head and summed over heads -- "The Dispatch Wire:
+ *    Connecting a Triton Indexer Kernel to Production Inference", section
+ *    "The Road to This Message", and the fp8-to-bf16 cast / ReLU / weighted
+ *    head sum / per-position scale listed in its section "Assumptions and
+ *    Risks";
+ *  - keys stored per cache block as 64 positions of 128 fp8 values followed
+ *    by 64 fp32 scales -- same page, section "The Reasoning and
+ *    Decision-Making";
+ *  - bf16 keys at 256 bytes per position with no quantisation -- "The Dispatch
+ *    Decision: Wiring a Triton Kernel into Production", section "The Problem
+ *    That Led Here";
+ *  - positions at or past the row's length are -inf -- "The Final Gate:
+ *    Validating a Custom Triton Indexer Kernel Before Production Deployment",
+ *    section "What the Test Output Reveals".
+ *
+ * Readings where the pages are silent (each is listed in the design notes):
+ *  - fp8 means OCP e4m3fn (bias 7, no infinities, S.1111.111 is NaN, largest
+ *    finite 448); the pages only say "fp8";
+ *  - ReLU(x) = max(x, 0) with NaN propagated (the fallback's clamp_min);
+ *  - the scale multiplies the dot product before the ReLU;
+ *  - L = clamp(seqlen, 0, table_width*64);
+ *  - a page id that must be read and lies outside [0, num_pages) yields NaN at
+ *    that page's live positions.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* OCP 8-bit floating point, E4M3 ("fn": finite, no infinities).
+ * sign s, 4-bit exponent e (bias 7), 3-bit mantissa m:
+ *   e == 0            : (-1)^s * 2^-6 * (m / 8)        (subnormal)
+ *   e == 15 && m == 7 : NaN
+ *   otherwise         : (-1)^s * 2^(e-7) * (1 + m / 8)                      */
+double oracle_e4m3fn_value(uint32_t code) {
+  const uint32_t s = (code >> 7) & 1u, e = (code >> 3) & 15u, m = code & 7u;
+  double mag;
+  if (e == 15u && m == 7u) return NAN;
+  if (e == 0u)
+    mag = ldexp((double)m / 8.0, -6);
+  else
+    mag = ldexp(1.0 + (double)m / 8.0, (int)e - 7);
+  return s ? -mag : mag;
+}
+
+/* bfloat16: the upper 16 bits of an IEEE binary32. */
+double oracle_bf16_value(uint16_t bits) {
+  const uint32_t u = (uint32_t)bits << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+static double relu(double x) { return isnan(x) ? x : (x > 0.0 ? x : 0.0); }
+
+enum { NH = 64, HD = 128, PG = 64 };
+
+/*
+ * Full definition over host buffers laid out exactly as the library's
+ * arguments (see the library header).  key_kind 0 = e4m3fn keys with scales,
+ * 1 = bf16 keys with s = 1.
+ *
+ *   q_bits      bf16 bits [rows][64][128]
+ *   kv          key pool bytes; page g at kv + g*kv_stride
+ *   ks          scale bytes (fp8 only); scale (g, i) at ks + g*ks_stride + 4*i
+ *   page_table  int32; row b's table at page_table + b*pt_stride
+ *   seqlens     int32 [rows]
+ *   weights     fp32 [rows][64]
+ *   row_ids     rows to evaluate (n_out of them); NULL = all rows in order
+ *   out         float64 [n_out][table_width*64]
+ */
+void oracle_paged_mqa_logits(int key_kind, const uint16_t* q_bits, const uint8_t* kv,
+                             int64_t kv_stride, const uint8_t* ks, int64_t ks_stride,
+                             int64_t num_pages, const int32_t* page_table, int64_t pt_stride,
+                             const int32_t* seqlens, const float* weights, int32_t rows,
+                             int32_t table_width, const int32_t* row_ids, int32_t n_out,
+                             double* out) {
+  const int64_t ncols = (int64_t)table_width * PG;
+  if (row_ids == NULL) n_out = rows;
+  const int64_t total = (int64_t)n_out * table_width;
+
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t t = 0; t < total; ++t) {
+    const int32_t r = (int32_t)(t / table_width);
+    const int32_t j = (int32_t)(t % table_width);
+    const int32_t b = row_ids ? row_ids[r] : r;
+    double* o = out + (int64_t)r * ncols + (int64_t)j * PG;
+
+    int64_t L = seqlens[b];
+    if (L < 0) L = 0;
+    if (L > ncols) L = ncols;
+
+    if ((int64_t)j * PG >= L) {            /* whole page past the length */
+      for (int i = 0; i < PG; ++i) o[i] = -INFINITY;
+      continue;
+    }
+    const int32_t g = page_table[(int64_t)b * pt_stride + j];
+    const int page_ok = (g >= 0 && (int64_t)g < num_pages);
+
+    for (int i = 0; i < PG; ++i) {
+      const int64_t p = (int64_t)j * PG + i;
+      if (p >= L) { o[i] = -INFINITY; continue; }
+      if (!page_ok) { o[i] = NAN; continue; }
+
+      double k[HD];
+      double s;
+      if (key_kind == 0) {
+        const uint8_t* kp = kv + (int64_t)g * kv_stride + (int64_t)i * HD;
+        for (int d = 0; d < HD; ++d) k[d] = oracle_e4m3fn_value(kp[d]);
+        float sf;
+        memcpy(&sf, ks + (int64_t)g * ks_stride + 4 * i, sizeof sf);
+        s = (double)sf;
+      } else {
+        const uint8_t* kp = kv + (int64_t)g * kv_stride + (int64_t)i * HD * 2;
+        for (int d = 0; d < HD; ++d) {
+          uint16_t bits;
+          memcpy(&bits, kp + 2 * d, sizeof bits);
+          k[d] = oracle_bf16_value(bits);
+        }
+        s = 1.0;
+      }
+
+      double acc = 0.0;
+      for (int h = 0; h < NH; ++h) {
+        const uint16_t* qh = q_bits + ((int64_t)b * NH + h) * HD;
+        double dot = 0.0;
+        for (int d = 0; d < HD; ++d) dot += oracle_bf16_value(qh[d]) * k[d];
+        acc += (double)weights[(int64_t)b * NH + h] * relu(s * dot);
+      }
+      o[i] = acc;
+    }
+  }
+}
+
+/* Number of OpenMP threads the oracle runs with (1 when built without it). */
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* Set the OpenMP thread count used by later calls (no-op without OpenMP). */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
