@@ -1,0 +1,294 @@
+"""Benchmark of the paged MQA-logits indexer on one MI355X.
+
+Default workload: fp8 decode with a 4097-page table (262,208 c4-positions per
+row), 64 rows, lengths uniform in [512, 32768] -- the configuration on which the
+HBM-bandwidth target and the O(actual length) claim are judged.  One step = one
+library call over the whole batch (grid/early exit, page lookup, key gather,
+fp8->bf16, MFMA, scale/ReLU/weighted head sum, masked store).
+
+Prints ONE JSON line:
+  value          c4-positions scored per second (live positions only), whole job
+  roofline       HBM roofline of the kernel: algorithmic bytes per launch / mean
+                 launch time (HIP events on the launch stream) vs 8 TB/s
+  cpu_baseline   the CPU oracle timed on a bounded row sample of the same workload
+  secondary      same measurements for the 128-page decode, the 513-slot control
+                 of the default workload, and the bf16 prefill (MFMA roofline)
+
+Inputs are synthetic and seeded (workloads.py).  Key pools and outputs are
+rotated over enough copies that one launch's bytes are gone from the 256 MB
+last-level cache by the time the copy is read again.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+KERNEL_SOURCE = ROOT / "paged_mqa_logits_idx_amd" / "csrc" / "paged_mqa_logits.hip"
+TRAFFIC_FILE = ROOT / "profiles" / "traffic.json"
+ROTATE_BYTES = 1 << 30           # >= 4x the 256 MB last-level cache
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_sha() -> str:
+    return hashlib.sha256(KERNEL_SOURCE.read_bytes()).hexdigest()[:16]
+
+
+def algorithmic_work(wl):
+    """Bytes the method must move and FLOPs it must do for one call.
+
+    Reads: live key values + scales (132 B/position fp8, 256 B bf16), each
+    row's query (16 KiB) and weights (256 B) and length (4 B), one table entry
+    per live page.  Writes: the whole fixed-shape output (4 B per slot).
+    FLOPs: 2 * 64 * 128 per live (row, position) pair.
+    """
+    import workloads as W
+    live = wl.live_positions()
+    per_pos = (W.HEAD_DIM + 4) if wl.key_kind == "fp8" else 2 * W.HEAD_DIM
+    reads = live * per_pos + wl.rows * (W.NUM_HEADS * W.HEAD_DIM * 2 + W.NUM_HEADS * 4 + 4) \
+        + 4 * wl.live_pages()
+    if wl.pt_stride == 0:  # one shared table and one key set for every row
+        L = int(wl.lengths().max())
+        reads = L * per_pos + wl.rows * (W.NUM_HEADS * W.HEAD_DIM * 2 + W.NUM_HEADS * 4 + 4) \
+            + 4 * ((L + W.PAGE - 1) // W.PAGE)
+    writes = wl.rows * wl.ncols * 4
+    flops = 2 * W.NUM_HEADS * W.HEAD_DIM * live
+    return reads, writes, flops
+
+
+def measure(cfg, steps: int, warmup: int):
+    """Time `steps` back-to-back library calls on one GPU."""
+    import torch
+
+    import paged_mqa_logits_idx_amd as lib
+    import workloads as W
+
+    t0 = time.perf_counter()
+    wl = W.config(cfg)
+    log(f"config {cfg}: generated in {time.perf_counter() - t0:.1f}s "
+        f"({wl.live_positions()} live positions)")
+    base = W.to_device(wl)
+    per_set = base.kv.numel() + base.out.numel() * 4 + base.q.numel() * 2
+    n_sets = max(2, min(64, math.ceil(ROTATE_BYTES / per_set)))
+    sets = [base]
+    for _ in range(n_sets - 1):
+        d = W.DeviceWorkload(**{**base.__dict__})
+        d.kv = base.kv.clone()
+        d.q = base.q.clone()
+        d.out = torch.empty_like(base.out)
+        if wl.key_kind == "fp8":
+            if wl.fused:
+                d.kscale_addr = d.kv.data_ptr() + wl.ks_offset
+            else:
+                d.ks = base.ks.clone()
+                d.kscale_addr = d.ks.data_ptr() + wl.ks_offset
+        sets.append(d)
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        W.run_library(sets[i % n_sets], lib, stream=stream)
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    region_s, region_e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    region_s.record(stream)
+    for i in range(steps):
+        starts[i].record(stream)
+        W.run_library(sets[i % n_sets], lib, stream=stream)
+        ends[i].record(stream)
+    region_e.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    per_launch = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    region_ms = region_s.elapsed_time(region_e)
+    reads, writes, flops = algorithmic_work(wl)
+    mean_ms = sum(per_launch) / len(per_launch)
+    srt = sorted(per_launch)
+    res = {
+        "cfg": cfg, "name": wl.name, "rows": wl.rows, "table_width": wl.table_width,
+        "key_kind": wl.key_kind, "live_positions": wl.live_positions(),
+        "live_pages": wl.live_pages(), "sets": n_sets,
+        "kernel_ms_mean": mean_ms, "kernel_ms_p10": srt[len(srt) // 10],
+        "kernel_ms_p50": srt[len(srt) // 2], "kernel_ms_p90": srt[(9 * len(srt)) // 10],
+        "region_ms": region_ms, "wall_s": wall, "steps": steps,
+        "alg_read_bytes": reads, "alg_write_bytes": writes, "alg_flops": flops,
+        "gbs": (reads + writes) / (mean_ms * 1e-3) / 1e9,
+        "tflops": flops / (mean_ms * 1e-3) / 1e12,
+        "positions_per_s_kernel": wl.live_positions() / (mean_ms * 1e-3),
+    }
+    del sets, base
+    torch.cuda.empty_cache()
+    return wl, res
+
+
+def cpu_baseline(wl, target_s: float):
+    """The oracle, as it stands, on a bounded sample of rows of the same workload."""
+    import numpy as np
+
+    import oracle
+
+    ora = oracle.default()
+    L = wl.lengths()
+    order = list(np.random.default_rng(0).permutation(wl.rows))
+    t = time.perf_counter()
+    ora.paged_mqa_logits(wl, rows=[order[0]])
+    first = time.perf_counter() - t
+    per_pos = first / max(1, int(L[order[0]]))
+    budget_pos = target_s / max(per_pos, 1e-12)
+    rows, acc = [], 0
+    for r in order:
+        if rows and acc + int(L[r]) > budget_pos:
+            break
+        rows.append(int(r))
+        acc += int(L[r])
+    t = time.perf_counter()
+    ora.paged_mqa_logits(wl, rows=rows)
+    el = time.perf_counter() - t
+    return {
+        "value": acc / el, "unit": "c4-positions/s", "cores": ora.num_threads(),
+        "kind": "oracle",
+        "sample": f"{len(rows)} of {wl.rows} rows of the default workload "
+                  f"({acc} live positions, float64, {el:.1f} s)",
+    }
+
+
+def traffic_for(cfg_key: str, launches_alg_bytes: float):
+    """HBM bytes per launch from committed rocprofv3 counters, if taken on this kernel source."""
+    if not TRAFFIC_FILE.exists():
+        return None
+    data = json.loads(TRAFFIC_FILE.read_text())
+    ent = data.get(cfg_key)
+    if not ent or ent.get("kernel_sha") != kernel_sha():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="3", help="configuration: 0-4 or 3c (default 3)")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a device copy of 1 GiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; the indexer needs no "
+                                   "cross-GPU exchange and is measured at N=1"}))
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        return 2
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log("copied 1 GiB x5")
+        return 0
+
+    cfg = args.workload if args.workload == "3c" else int(args.workload)
+    wl, main_res = measure(cfg, args.steps, args.warmup)
+    log(json.dumps(main_res))
+
+    secondary = {}
+    if not args.no_secondary:
+        for c in (2, "3c", 4):
+            if str(c) == str(cfg):
+                continue
+            _, r = measure(c, max(10, args.steps // 2), max(3, args.warmup // 2))
+            log(json.dumps(r))
+            entry = {
+                "workload": r["name"], "kernel_ms_mean": round(r["kernel_ms_mean"], 5),
+                "positions_per_s": r["positions_per_s_kernel"],
+            }
+            if r["key_kind"] == "bf16":
+                entry.update(bound="mfma", achieved_tflops=round(r["tflops"], 2),
+                             peak_tflops=BF16_MFMA_PEAK_TFLOPS,
+                             frac=round(r["tflops"] / BF16_MFMA_PEAK_TFLOPS, 4),
+                             alg_flops=r["alg_flops"])
+            else:
+                entry.update(bound="hbm", achieved_gbs=round(r["gbs"], 1), peak_gbs=HBM_PEAK_GBS,
+                             frac=round(r["gbs"] / HBM_PEAK_GBS, 4),
+                             alg_bytes=r["alg_read_bytes"] + r["alg_write_bytes"])
+            secondary[str(c)] = entry
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a row sample")
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+
+    steps = args.steps
+    ms_per_step = main_res["region_ms"] / steps
+    value = main_res["live_positions"] / (ms_per_step * 1e-3)
+    alg_bytes = main_res["alg_read_bytes"] + main_res["alg_write_bytes"]
+    achieved = alg_bytes / (main_res["kernel_ms_mean"] * 1e-3) / 1e9
+    traffic = traffic_for(str(cfg), alg_bytes)
+    out = {
+        "metric": "indexer c4-positions scored/sec + achieved HBM GB/s (decode) / MFMA % (prefill)",
+        "value": value,
+        "unit": "c4-positions/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; q bf16 N(0,1), w N(0,1)/8, keys e4m3fn from N(0,1) "
+                "with per-position scale amax/448)",
+        "config": {
+            "workload": main_res["name"],
+            "rows": main_res["rows"],
+            "table_width_pages": main_res["table_width"],
+            "positions_per_row": main_res["table_width"] * 64,
+            "seqlens": "uniform [512, 32768]" if str(cfg) in ("3", "3c") else "see workloads.py",
+            "live_positions_per_step": main_res["live_positions"],
+            "key_format": "e4m3fn + fp32 scale, 8448-byte blocks" if main_res["key_kind"] == "fp8"
+                          else "bf16, 16384-byte pages",
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "alg_bytes_per_launch": alg_bytes,
+            "kernel_ms_mean": round(main_res["kernel_ms_mean"], 5),
+            "kernel_ms_p50": round(main_res["kernel_ms_p50"], 5),
+        },
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

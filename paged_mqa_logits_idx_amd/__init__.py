@@ -1,0 +1,173 @@
+"""Python binding of the paged MQA-logits indexer library (libidx_paged_mqa.so).
+
+Argument marshalling only: every step of the computation runs in the library's
+HIP kernels.  The functions carry the C-ABI names and argument order; they
+accept torch device tensors (or raw device addresses as ints) and pass their
+addresses and sizes through ctypes.  torch supplies device memory and streams.
+
+The library must be built in-tree first (``python -m paged_mqa_logits_idx_amd._build``
+or ``__graft_entry__.build()``); importing this module without it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+import torch  # loads the HIP runtime the library binds to (same soname)
+
+LIB_PATH = Path(__file__).resolve().parent / "libidx_paged_mqa.so"
+
+NUM_HEADS = 64
+HEAD_DIM = 128
+PAGE_POSITIONS = 64
+FP8_PAGE_KEY_BYTES = PAGE_POSITIONS * HEAD_DIM          # 8192
+FP8_PAGE_SCALE_BYTES = PAGE_POSITIONS * 4               # 256
+FP8_FUSED_PAGE_BYTES = FP8_PAGE_KEY_BYTES + FP8_PAGE_SCALE_BYTES  # 8448
+BF16_PAGE_BYTES = PAGE_POSITIONS * HEAD_DIM * 2         # 16384
+
+IDX_OK = 0
+IDX_ERR_NULL = -1
+IDX_ERR_UNSUPPORTED = -2
+IDX_ERR_SHAPE = -3
+IDX_ERR_ALIGN = -4
+IDX_ERR_LAUNCH = -5
+
+_SYMBOLS = (
+    "idx_paged_mqa_logits_fp8",
+    "idx_paged_mqa_logits_bf16",
+    "idx_status_string",
+    "idx_abi_version",
+)
+
+
+class IdxError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{msg} (status {status})")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not LIB_PATH.exists():
+        raise ImportError(
+            f"{LIB_PATH} is missing: build the HIP library first "
+            "(python -m paged_mqa_logits_idx_amd._build)")
+    lib = ctypes.CDLL(str(LIB_PATH))
+    argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+        ctypes.c_void_p,
+    ]
+    for name in ("idx_paged_mqa_logits_fp8", "idx_paged_mqa_logits_bf16"):
+        fn = getattr(lib, name)
+        fn.argtypes = argtypes
+        fn.restype = ctypes.c_int
+    lib.idx_status_string.argtypes = [ctypes.c_int]
+    lib.idx_status_string.restype = ctypes.c_char_p
+    lib.idx_abi_version.argtypes = []
+    lib.idx_abi_version.restype = ctypes.c_int
+    return lib
+
+
+_lib = _load()
+
+
+def idx_status_string(status: int) -> str:
+    return _lib.idx_status_string(int(status)).decode()
+
+
+def idx_abi_version() -> int:
+    return int(_lib.idx_abi_version())
+
+
+def _addr(x) -> int | None:
+    if x is None:
+        return None
+    if isinstance(x, torch.Tensor):
+        if x.device.type != "cuda":
+            raise ValueError("tensors passed to the indexer library must be device tensors")
+        return x.data_ptr()
+    return int(x)
+
+
+def _stream_handle(stream, device) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream(device).cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _call(name, q, kv_pages, kscale, page_table, seqlens, weights, out, *, rows, num_heads,
+          head_dim, table_width, num_pages, kv_page_stride, kscale_page_stride,
+          page_table_row_stride, stream, check):
+    dev = q.device if isinstance(q, torch.Tensor) else None
+    fn = getattr(_lib, name)
+    status = fn(_addr(q), _addr(kv_pages), _addr(kscale), _addr(page_table), _addr(seqlens),
+                _addr(weights), _addr(out), int(rows), int(num_heads), int(head_dim),
+                int(table_width), int(num_pages), int(kv_page_stride), int(kscale_page_stride),
+                int(page_table_row_stride), _stream_handle(stream, dev))
+    if check and status != IDX_OK:
+        raise IdxError(status, f"{name}: {idx_status_string(status)}")
+    return status
+
+
+def _dims(q, page_table, table_width, rows, num_heads, head_dim, page_table_row_stride):
+    if isinstance(q, torch.Tensor):
+        if rows is None:
+            rows = q.shape[0]
+        if num_heads is None:
+            num_heads = q.shape[1] if q.dim() == 3 else NUM_HEADS
+        if head_dim is None:
+            head_dim = q.shape[2] if q.dim() == 3 else HEAD_DIM
+    if table_width is None:
+        if not (isinstance(page_table, torch.Tensor) and page_table.dim() == 2):
+            raise ValueError("table_width is required unless page_table is a 2-D tensor")
+        table_width = page_table.shape[1]
+    if page_table_row_stride is None:
+        if not (isinstance(page_table, torch.Tensor) and page_table.dim() == 2):
+            raise ValueError("page_table_row_stride is required unless page_table is a 2-D tensor")
+        page_table_row_stride = 0 if page_table.shape[0] == 1 and rows != 1 else page_table.stride(0)
+    return rows, num_heads, head_dim, table_width, page_table_row_stride
+
+
+def idx_paged_mqa_logits_fp8(q, kv_pages, kscale, page_table, seqlens, weights, out, *,
+                             num_pages, kv_page_stride=FP8_FUSED_PAGE_BYTES,
+                             kscale_page_stride=FP8_FUSED_PAGE_BYTES, table_width=None,
+                             page_table_row_stride=None, rows=None, num_heads=None,
+                             head_dim=None, stream=None, check=True) -> int:
+    """out[b, p] = sum_h w[b,h] * ReLU(s_p * <q[b,h], k_p>) for p < seqlens[b], else -inf.
+
+    fp8 (e4m3fn) keys with a per-position fp32 scale.  ``kscale`` is a tensor or
+    a device address; for the fused 8448-byte block pass
+    ``kv_pages.data_ptr() + 8192``.  Returns the library status (raises
+    IdxError on failure when ``check``).
+    """
+    rows, num_heads, head_dim, table_width, pts = _dims(
+        q, page_table, table_width, rows, num_heads, head_dim, page_table_row_stride)
+    return _call("idx_paged_mqa_logits_fp8", q, kv_pages, kscale, page_table, seqlens, weights,
+                 out, rows=rows, num_heads=num_heads, head_dim=head_dim, table_width=table_width,
+                 num_pages=num_pages, kv_page_stride=kv_page_stride,
+                 kscale_page_stride=kscale_page_stride, page_table_row_stride=pts, stream=stream,
+                 check=check)
+
+
+def idx_paged_mqa_logits_bf16(q, kv_pages, kscale, page_table, seqlens, weights, out, *,
+                              num_pages, kv_page_stride=BF16_PAGE_BYTES, kscale_page_stride=0,
+                              table_width=None, page_table_row_stride=None, rows=None,
+                              num_heads=None, head_dim=None, stream=None, check=True) -> int:
+    """Same as :func:`idx_paged_mqa_logits_fp8` with bf16 keys and s_p = 1 (kscale must be None)."""
+    rows, num_heads, head_dim, table_width, pts = _dims(
+        q, page_table, table_width, rows, num_heads, head_dim, page_table_row_stride)
+    return _call("idx_paged_mqa_logits_bf16", q, kv_pages, kscale, page_table, seqlens, weights,
+                 out, rows=rows, num_heads=num_heads, head_dim=head_dim, table_width=table_width,
+                 num_pages=num_pages, kv_page_stride=kv_page_stride,
+                 kscale_page_stride=kscale_page_stride, page_table_row_stride=pts, stream=stream,
+                 check=check)
+
+
+__all__ = [
+    "idx_paged_mqa_logits_fp8", "idx_paged_mqa_logits_bf16", "idx_status_string",
+    "idx_abi_version", "IdxError", "LIB_PATH", "NUM_HEADS", "HEAD_DIM", "PAGE_POSITIONS",
+]

@@ -1,0 +1,109 @@
+"""The C-ABI library loads on the CPU host and exports what the header declares.
+
+No kernel is launched here: only entry points whose arguments fail host-side
+validation are called, and those return before any HIP call.
+"""
+import ctypes
+import re
+import subprocess
+from pathlib import Path
+
+import pytest
+
+ROOT = Path(__file__).resolve().parent.parent
+HEADER = ROOT / "include" / "paged_mqa_logits.h"
+LIB = ROOT / "paged_mqa_logits_idx_amd" / "libidx_paged_mqa.so"
+
+IDX_OK, IDX_ERR_NULL, IDX_ERR_UNSUPPORTED, IDX_ERR_SHAPE, IDX_ERR_ALIGN = 0, -1, -2, -3, -4
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(idx_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not LIB.exists():
+        pytest.fail(f"{LIB} not built (run __graft_entry__.build())")
+    l = ctypes.CDLL(str(LIB))
+    args = [ctypes.c_void_p] * 7 + [ctypes.c_int32] * 4 + [ctypes.c_int64] * 4 + [ctypes.c_void_p]
+    for name in ("idx_paged_mqa_logits_fp8", "idx_paged_mqa_logits_bf16"):
+        getattr(l, name).argtypes = args
+        getattr(l, name).restype = ctypes.c_int
+    l.idx_status_string.restype = ctypes.c_char_p
+    l.idx_status_string.argtypes = [ctypes.c_int]
+    return l
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted([
+        "idx_abi_version", "idx_paged_mqa_logits_bf16", "idx_paged_mqa_logits_fp8",
+        "idx_status_string"])
+
+
+def test_every_declared_symbol_is_exported(lib):
+    dyn = subprocess.run(["nm", "-D", "--defined-only", str(LIB)], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (idx_[a-z0-9_]+)$", dyn, flags=re.M))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.idx_abi_version() == 1
+    for st in (IDX_OK, IDX_ERR_NULL, IDX_ERR_UNSUPPORTED, IDX_ERR_SHAPE, IDX_ERR_ALIGN, -5, 99):
+        assert isinstance(lib.idx_status_string(st), bytes) and lib.idx_status_string(st)
+
+
+def _call(lib, name, **kw):
+    a = dict(q=16, kv=16, ks=16, pt=4, sl=4, w=16, out=16, rows=1, heads=64, dim=128, width=1,
+             num_pages=1, kv_stride=8448, ks_stride=8448, pt_stride=1)
+    if name.endswith("bf16"):
+        a.update(ks=None, kv_stride=16384, ks_stride=0)
+    a.update(kw)
+    fn = getattr(lib, name)
+    return fn(a["q"], a["kv"], a["ks"], a["pt"], a["sl"], a["w"], a["out"], a["rows"],
+              a["heads"], a["dim"], a["width"], a["num_pages"], a["kv_stride"], a["ks_stride"],
+              a["pt_stride"], None)
+
+
+FP8, BF16 = "idx_paged_mqa_logits_fp8", "idx_paged_mqa_logits_bf16"
+
+
+@pytest.mark.parametrize("name,kw,status", [
+    (FP8, dict(heads=32), IDX_ERR_UNSUPPORTED),
+    (FP8, dict(dim=64), IDX_ERR_UNSUPPORTED),
+    (BF16, dict(heads=128), IDX_ERR_UNSUPPORTED),
+    (FP8, dict(rows=-1), IDX_ERR_SHAPE),
+    (FP8, dict(width=-1), IDX_ERR_SHAPE),
+    (FP8, dict(width=(1 << 24) + 1), IDX_ERR_SHAPE),
+    (FP8, dict(num_pages=-1), IDX_ERR_SHAPE),
+    (FP8, dict(pt_stride=-1), IDX_ERR_SHAPE),
+    (FP8, dict(kv_stride=8191), IDX_ERR_SHAPE),
+    (FP8, dict(ks_stride=255), IDX_ERR_SHAPE),
+    (BF16, dict(kv_stride=8448), IDX_ERR_SHAPE),
+    (FP8, dict(rows=0, q=None, kv=None), IDX_OK),          # nothing to do: no launch
+    (FP8, dict(width=0, out=None), IDX_OK),
+    (FP8, dict(q=None), IDX_ERR_NULL),
+    (FP8, dict(kv=None), IDX_ERR_NULL),
+    (FP8, dict(ks=None), IDX_ERR_NULL),
+    (FP8, dict(pt=None), IDX_ERR_NULL),
+    (FP8, dict(sl=None), IDX_ERR_NULL),
+    (FP8, dict(w=None), IDX_ERR_NULL),
+    (FP8, dict(out=None), IDX_ERR_NULL),
+    (BF16, dict(ks=16), IDX_ERR_NULL),                       # bf16 takes no scales
+    (FP8, dict(q=8), IDX_ERR_ALIGN),
+    (FP8, dict(kv=32 + 4), IDX_ERR_ALIGN),
+    (FP8, dict(out=4), IDX_ERR_ALIGN),
+    (FP8, dict(w=20), IDX_ERR_ALIGN),
+    (FP8, dict(pt=2), IDX_ERR_ALIGN),
+    (FP8, dict(sl=6), IDX_ERR_ALIGN),
+    (FP8, dict(ks=18), IDX_ERR_ALIGN),
+    (FP8, dict(kv_stride=8456), IDX_ERR_ALIGN),
+    (FP8, dict(ks_stride=8450), IDX_ERR_ALIGN),
+])
+def test_host_validation(lib, name, kw, status):
+    assert _call(lib, name, **kw) == status
