@@ -51,6 +51,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef __attribute__((address_space(1))) const void* global_ptr;
 
 struct Params {
   const uint8_t* q;   // bf16 [rows][64][128]
@@ -65,12 +68,13 @@ struct Params {
 };
 
 // Raw key bytes of one page for one lane, already in B-fragment order:
-// 4 position blocks (nb) x 32 k-values.  fp8: 32 bytes per nb; bf16: 64.
+// 4 position blocks (nb) x 32 k-values (fp8: 32 bytes per nb; bf16: 64), and
+// the scale of position `lane` of the page (1 for bf16).
 template <int KEY>
 struct PageKeys {
   static constexpr int kVec = (KEY == kFp8) ? 2 : 4;  // u32x4 per nb
   u32x4 v[4][kVec];
-  float s[4];  // scale of position 16*nb + n (1 for bf16)
+  float s;
 };
 
 __device__ __forceinline__ uint32_t bits_of(bf16x2 x) { return __builtin_bit_cast(uint32_t, x); }
@@ -116,14 +120,10 @@ __device__ __forceinline__ void load_page_global(const Params& p, int32_t gp, in
 #pragma unroll
     for (int v = 0; v < PageKeys<KEY>::kVec; ++v) pk.v[nb][v] = __builtin_nontemporal_load(src + v);
   }
-  if constexpr (KEY == kFp8) {
-    const float* sc = reinterpret_cast<const float*>(p.ks + (int64_t)gp * p.ks_stride);
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) pk.s[nb] = sc[16 * nb + n];
-  } else {
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) pk.s[nb] = 1.0f;
-  }
+  if constexpr (KEY == kFp8)
+    pk.s = reinterpret_cast<const float*>(p.ks + (int64_t)gp * p.ks_stride)[lane];
+  else
+    pk.s = 1.0f;
 }
 
 // Score one page: returns the logit of position 64*j + lane (before masking).
@@ -131,43 +131,96 @@ __device__ __forceinline__ void load_page_global(const Params& p, int32_t gp, in
 //   logit_i  = |s_i| * sum_h w[h] * ReLU(x')      with x' = x for s_i >= 0 and
 //              x' = -x (keys negated, exact) for s_i < 0, which equals
 //              sum_h w[h] * ReLU(s_i * x) in exact arithmetic.
-template <int KEY>
-__device__ __forceinline__ float score_page(const RowQuery& rq, const PageKeys<KEY>& pk, int lane) {
-  const int g = lane >> 4;
-  float res[4];
+// Lane l = 16*g + n holds, per position block nb, the partial sum over its 16
+// heads of position 16*nb + n; a two-step butterfly (xor 16, xor 32) leaves lane
+// l with the full head sum of position 16*g + n = l.
+// B operands of position block nb (8 bf16 per k-slice), keys negated when
+// FLIP says the position's scale is negative.
+template <int KEY, bool FLIP>
+__device__ __forceinline__ void block_operands(const PageKeys<KEY>& pk, int nb, int n,
+                                               bf16x8 (&kop)[4]) {
+  if constexpr (KEY == kFp8) {
+    uint32_t flip = 0;
+    if constexpr (FLIP) flip = (__shfl(pk.s, 16 * nb + n) < 0.0f) ? 0x80808080u : 0u;
+    kop[0] = fp8x8_to_bf16x8(pk.v[nb][0].x ^ flip, pk.v[nb][0].y ^ flip);
+    kop[1] = fp8x8_to_bf16x8(pk.v[nb][0].z ^ flip, pk.v[nb][0].w ^ flip);
+    kop[2] = fp8x8_to_bf16x8(pk.v[nb][1].x ^ flip, pk.v[nb][1].y ^ flip);
+    kop[3] = fp8x8_to_bf16x8(pk.v[nb][1].z ^ flip, pk.v[nb][1].w ^ flip);
+  } else {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) kop[kb] = __builtin_bit_cast(bf16x8, pk.v[nb][kb]);
+  }
+}
+
+// sum over the lane's 16 heads of w[h] * ReLU(x[h]) for one position block
+__device__ __forceinline__ float block_epilogue(const RowQuery& rq, const f32x4 (&acc)[4]) {
+  float sum = 0.f;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      sum = fmaf(rq.w[mb][r], __builtin_elementwise_maximum(acc[mb][r], 0.0f), sum);
+  return sum;
+}
+
+// Score one page: returns the logit of position 64*j + lane (before masking).
+//   x[h][i]  = <q[h], k_i>                       (MFMA, fp32 accumulate)
+//   logit_i  = |s_i| * sum_h w[h] * ReLU(x')      with x' = x for s_i >= 0 and
+//              x' = -x (keys negated, exact) for s_i < 0, which equals
+//              sum_h w[h] * ReLU(s_i * x) in exact arithmetic.
+// The four position blocks are software-pipelined: while the 16 MFMAs of
+// block nb run, the VALU converts block nb+1 and reduces block nb-1.
+// Lane l = 16*g + n then holds, per block nb, the partial sum over its 16 heads
+// of position 16*nb + n; a two-step butterfly (xor 16, xor 32) leaves lane l
+// with the full head sum of position 16*g + n = l.
+template <int KEY, bool FLIP>
+__device__ __forceinline__ float score_page_impl(const RowQuery& rq, const PageKeys<KEY>& pk,
+                                                 int lane) {
+  const int n = lane & 15, g = lane >> 4;
+  bf16x8 kop[2][4];
+  f32x4 acc[2][4];
+  float part[4];
+  block_operands<KEY, FLIP>(pk, 0, n, kop[0]);
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
-    bf16x8 kop[4];
-    if constexpr (KEY == kFp8) {
-      const uint32_t flip = (__builtin_bit_cast(uint32_t, pk.s[nb]) >> 31) * 0x80808080u;
-      kop[0] = fp8x8_to_bf16x8(pk.v[nb][0].x ^ flip, pk.v[nb][0].y ^ flip);
-      kop[1] = fp8x8_to_bf16x8(pk.v[nb][0].z ^ flip, pk.v[nb][0].w ^ flip);
-      kop[2] = fp8x8_to_bf16x8(pk.v[nb][1].x ^ flip, pk.v[nb][1].y ^ flip);
-      kop[3] = fp8x8_to_bf16x8(pk.v[nb][1].z ^ flip, pk.v[nb][1].w ^ flip);
-    } else {
+    const int cur = nb & 1;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) kop[kb] = __builtin_bit_cast(bf16x8, pk.v[nb][kb]);
-    }
-    f32x4 acc[4];
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) acc[mb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int mb = 0; mb < 4; ++mb) acc[cur][mb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
-        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rq.a[mb][kb], kop[kb], acc[mb], 0, 0, 0);
-    float part = 0.f;
+        acc[cur][mb] =
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(rq.a[mb][kb], kop[cur][kb], acc[cur][mb], 0, 0, 0);
+    if (nb + 1 < 4) block_operands<KEY, FLIP>(pk, nb + 1, n, kop[cur ^ 1]);
+    if (nb > 0) part[nb - 1] = block_epilogue(rq, acc[cur ^ 1]);
+    // interleave: each MFMA followed by up to 3 VALU ops (conversion of the
+    // next block, epilogue of the previous one)
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        part = fmaf(rq.w[mb][r], __builtin_elementwise_maximum(acc[mb][r], 0.0f), part);
-    part += __shfl_xor(part, 16);
-    part += __shfl_xor(part, 32);
-    res[nb] = (KEY == kFp8) ? fabsf(pk.s[nb]) * part : part;
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // 3 VALU
+    }
   }
-  // Lane l = 16*g + n owns position 16*g + n, i.e. block nb = g, column n.
-  return g == 0 ? res[0] : g == 1 ? res[1] : g == 2 ? res[2] : res[3];
+  part[3] = block_epilogue(rq, acc[1]);
+  // step 1 (partner g^1): keep blocks nb with nb%2 == g%2, send the others
+  const bool b0 = g & 1, b1 = g & 2;
+  const float keep0 = b0 ? part[1] : part[0], keep1 = b0 ? part[3] : part[2];
+  const float send0 = b0 ? part[0] : part[1], send1 = b0 ? part[2] : part[3];
+  const float t0 = keep0 + __shfl_xor(send0, 16);  // block g%2
+  const float t1 = keep1 + __shfl_xor(send1, 16);  // block g%2 + 2
+  // step 2 (partner g^2): keep block g
+  const float keep = b1 ? t1 : t0, send = b1 ? t0 : t1;
+  const float total = keep + __shfl_xor(send, 32);
+  return (KEY == kFp8) ? fabsf(pk.s) * total : total;
+}
+
+template <int KEY>
+__device__ __forceinline__ float score_page(const RowQuery& rq, const PageKeys<KEY>& pk, int lane) {
+  if constexpr (KEY == kFp8) {
+    if (__ballot(pk.s < 0.0f) != 0) return score_page_impl<KEY, true>(rq, pk, lane);
+  }
+  return score_page_impl<KEY, false>(rq, pk, lane);
 }
 
 __device__ __forceinline__ void store_page(float* orow, int32_t j, int32_t L, int lane, float v) {
@@ -195,11 +248,28 @@ __device__ __forceinline__ bool page_ok(int32_t gp, int64_t num_pages) {
   return gp >= 0 && (int64_t)gp < num_pages;
 }
 
+// Wave-uniform values kept in scalar registers.
+__device__ __forceinline__ int32_t uniform(int32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int64_t uniform(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Read of an int32 table (page tables, lengths) at a wave-uniform index
+// through the constant address space: a scalar load, counted by lgkmcnt, so it
+// never waits behind the key streams counted by vmcnt.  The tables are never
+// written by the kernels.
+__device__ __forceinline__ int32_t load_uniform(const int32_t* base, int64_t idx) {
+  typedef __attribute__((address_space(4))) const int32_t* const_i32;
+  return ((const_i32)(uintptr_t)base)[uniform(idx)];
+}
+
 // ---------------------------------------------------------------------------
 // rowwise kernel: unit = (row b, WAVES*PPW consecutive page slots); wave w of
 // the unit owns PPW slots.
 template <int KEY, int PPW, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) void rowwise_kernel(Params p, int32_t units_per_row,
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(KEY == kFp8 ? 2 : 1, 2))) void rowwise_kernel(Params p, int32_t units_per_row,
                                                               int64_t total_units) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -210,7 +280,7 @@ __global__ __launch_bounds__(64 * WAVES) void rowwise_kernel(Params p, int32_t u
     const int32_t j0 = (u * WAVES + wave) * PPW;
     if (j0 >= width) continue;
     const int32_t jend = min(j0 + PPW, width);
-    const int32_t L = clamp_len(p.sl[b], width);
+    const int32_t L = clamp_len(load_uniform(p.sl, b), width);
     const int32_t live = (L + kPage - 1) / kPage;
     const int32_t jl = max(j0, min(jend, live));  // [j0, jl) live, [jl, jend) dead
     float* orow = p.out + (int64_t)b * width * kPage;
@@ -220,7 +290,7 @@ __global__ __launch_bounds__(64 * WAVES) void rowwise_kernel(Params p, int32_t u
       load_row_query(p, b, lane, rq);
       const int32_t* tab = p.pt + (int64_t)b * p.pt_stride;
       PageKeys<KEY> buf[2];
-      int32_t gcur = tab[j0];
+      int32_t gcur = load_uniform(tab, j0);
       bool okcur = page_ok(gcur, p.num_pages);
       if (okcur) load_page_global<KEY>(p, gcur, lane, buf[0]);
 #pragma unroll
@@ -230,7 +300,7 @@ __global__ __launch_bounds__(64 * WAVES) void rowwise_kernel(Params p, int32_t u
           int32_t gnxt = 0;
           bool oknxt = false;
           if (t + 1 < PPW && j + 1 < jl) {
-            gnxt = tab[j + 1];
+            gnxt = load_uniform(tab, j + 1);
             oknxt = page_ok(gnxt, p.num_pages);
             if (oknxt) load_page_global<KEY>(p, gnxt, lane, buf[(t + 1) & 1]);
           }
@@ -244,6 +314,370 @@ __global__ __launch_bounds__(64 * WAVES) void rowwise_kernel(Params p, int32_t u
       }
     }
     if (jl < jend) fill_neg_inf(orow, jl, jend - jl, lane);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// balanced kernel: a fixed grid (about two workgroups per CU, set by the
+// scalar arguments and the device) in which every wave takes
+//   (1) an equal share of the row-major sequence of all rows' live pages,
+//       located from an in-wave prefix sum over the row lengths, and
+//   (2) an equal share of the (row, page slot) grid, of which it writes the
+//       slots past each row's live pages as -inf.
+// Dead slots cost no dispatch and the live work is spread evenly over the
+// SIMDs whatever the length mix.  Rows are scanned 64 at a time, so the
+// kernel serves batches of up to kBalancedMaxRows rows.
+constexpr int32_t kBalancedMaxRows = 1024;
+
+__device__ __forceinline__ int32_t live_pages_of(int32_t L) { return (L + kPage - 1) / kPage; }
+
+__device__ __forceinline__ int64_t wave_sum(int64_t v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
+  return v;
+}
+
+__device__ __forceinline__ int32_t wave_inclusive_scan(int32_t v, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int32_t t = __shfl_up(v, d);
+    if (lane >= d) v += t;
+  }
+  return v;
+}
+
+// Live pages [ja, jb) of row b (0 <= ja < jb <= live pages of the row).  Keys
+// of the next NBUF-1 pages are in flight while the current page is multiplied
+// (buffers rotate; every index is a compile-time constant after unrolling).
+template <int KEY, int NBUF>
+__device__ __forceinline__ void row_pages(const Params& p, int32_t b, int32_t ja, int32_t jb,
+                                          int32_t L, int lane) {
+  RowQuery rq;
+  load_row_query(p, b, lane, rq);
+  const int32_t* tab = p.pt + (int64_t)b * p.pt_stride;
+  float* orow = p.out + (int64_t)b * p.width * kPage;
+  PageKeys<KEY> buf[NBUF];
+  bool ok[NBUF];
+#pragma unroll
+  for (int t = 0; t < NBUF - 1; ++t) {
+    ok[t] = false;
+    if (ja + t < jb) {
+      const int32_t g = load_uniform(tab, ja + t);
+      ok[t] = page_ok(g, p.num_pages);
+      if (ok[t]) load_page_global<KEY>(p, g, lane, buf[t]);
+    }
+  }
+  for (int32_t j = ja; j < jb; j += NBUF) {
+#pragma unroll
+    for (int u = 0; u < NBUF; ++u) {
+      const int32_t jj = j + u;
+      if (jj < jb) {
+        constexpr int kAhead = NBUF - 1;
+        const int nxt = (u + kAhead) % NBUF;
+        if (jj + kAhead < jb) {
+          const int32_t g = load_uniform(tab, jj + kAhead);
+          ok[nxt] = page_ok(g, p.num_pages);
+          if (ok[nxt]) load_page_global<KEY>(p, g, lane, buf[nxt]);
+        }
+        if (ok[u])
+          store_page(orow, jj, L, lane, score_page<KEY>(rq, buf[u], lane));
+        else
+          store_bad_page(orow, jj, L, lane);
+      }
+    }
+  }
+}
+
+// ---- fp8 pages streamed HBM -> LDS with global_load_lds_dwordx4 ----------
+// Each wave owns two LDS slots of 8448 bytes.  DMA instruction t (0..7) copies
+// the contiguous kilobyte of key rows 8t..8t+7 (lane l: row 8t + l/8, 16-byte
+// chunk position l%8), so every instruction reads whole 128-byte lines.  The
+// slot keeps the rows in order but XOR-swizzles the chunks inside a row:
+// position c of row i holds key chunk c ^ (i % 8).  A B fragment then reads row
+// i = 16 nb + n, chunks 2g and 2g+1, at positions (2g+h) ^ (n % 8): the eight
+// lanes n = 0..7 of a lane group hit distinct banks.  The scales land at
+// slot + 8192 (lane l: scale of position l).  Per page: wait for the page's
+// DMA group, copy the slot into registers, refill the slot with the page two
+// ahead, multiply -- two pages are in flight during every multiply without
+// holding them in VGPRs.
+constexpr int kSlotBytes = 8448;
+constexpr int kDmaOps = 9;  // VMEM instructions per page (8 x 16 B + 1 x 4 B)
+// s_waitcnt immediate (gfx9 layout: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] |
+// vmcnt[5:4] << 14) waiting on vmcnt only.
+constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
+
+__device__ __forceinline__ void dma_page(const uint8_t* keys, const uint8_t* scales, lds_u8* slot,
+                                         int lane) {
+  const int rsub = lane >> 3, c = lane & 7;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int i = 8 * t + rsub;
+    const uint8_t* src = keys + i * kDim + 16 * (c ^ (i & 7));
+    __builtin_amdgcn_global_load_lds((global_ptr)src, (lds_ptr)(slot + 1024 * t), 16, 0, 0);
+  }
+  __builtin_amdgcn_global_load_lds((global_ptr)(scales + 4 * lane), (lds_ptr)(slot + 8192), 4, 0, 0);
+}
+
+// Lane's LDS byte offsets (within a slot) of its two 16-byte B chunks of
+// position block 0; block nb adds 2048 nb.
+__device__ __forceinline__ uint32_t slot_chunk_offset(int lane, int h) {
+  const int n = lane & 15, g = lane >> 4;
+  return (uint32_t)(n * kDim + 16 * ((2 * g + h) ^ (n & 7)));
+}
+
+// Wait until at most N vector-memory operations are outstanding (the page's
+// DMA group is then complete), then copy the slot into the lane's registers.
+// The compiler does not see these LDS reads, so it adds no conservative wait
+// for the other slot's DMA, which stays in flight.
+template <int N>
+__device__ __forceinline__ void read_slot(uint32_t a0, uint32_t a1, uint32_t a4, PageKeys<kFp8>& pk) {
+  asm volatile(
+      "s_waitcnt vmcnt(%12)\n\t"
+      "ds_read_b128 %0, %8\n\t"
+      "ds_read_b128 %1, %9\n\t"
+      "ds_read_b128 %2, %8 offset:2048\n\t"
+      "ds_read_b128 %3, %9 offset:2048\n\t"
+      "ds_read_b128 %4, %8 offset:4096\n\t"
+      "ds_read_b128 %5, %9 offset:4096\n\t"
+      "ds_read_b128 %6, %8 offset:6144\n\t"
+      "ds_read_b128 %7, %9 offset:6144\n\t"
+      "ds_read_b32 %10, %11\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(pk.v[0][0]), "=&v"(pk.v[0][1]), "=&v"(pk.v[1][0]), "=&v"(pk.v[1][1]),
+        "=&v"(pk.v[2][0]), "=&v"(pk.v[2][1]), "=&v"(pk.v[3][0]), "=&v"(pk.v[3][1]), "+v"(a0),
+        "+v"(a1), "=&v"(pk.s)
+      : "v"(a4), "n"(N)
+      : "memory");
+}
+
+// Wait until at most n_after vector-memory operations are outstanding (n_after
+// <= 31: up to 4 slots), then read the slot.
+__device__ __forceinline__ void read_slot_after(int n_after, uint32_t a0, uint32_t a1, uint32_t a4,
+                                                PageKeys<kFp8>& pk) {
+  switch (n_after) {
+    case 0: read_slot<0>(a0, a1, a4, pk); break;
+    case 1: read_slot<1>(a0, a1, a4, pk); break;
+    case 2: read_slot<2>(a0, a1, a4, pk); break;
+    case 3: read_slot<3>(a0, a1, a4, pk); break;
+    case 4: read_slot<4>(a0, a1, a4, pk); break;
+    case 5: read_slot<5>(a0, a1, a4, pk); break;
+    case 6: read_slot<6>(a0, a1, a4, pk); break;
+    case 7: read_slot<7>(a0, a1, a4, pk); break;
+    case 8: read_slot<8>(a0, a1, a4, pk); break;
+    case 9: read_slot<9>(a0, a1, a4, pk); break;
+    case 10: read_slot<10>(a0, a1, a4, pk); break;
+    case 11: read_slot<11>(a0, a1, a4, pk); break;
+    case 12: read_slot<12>(a0, a1, a4, pk); break;
+    case 13: read_slot<13>(a0, a1, a4, pk); break;
+    case 14: read_slot<14>(a0, a1, a4, pk); break;
+    case 15: read_slot<15>(a0, a1, a4, pk); break;
+    case 16: read_slot<16>(a0, a1, a4, pk); break;
+    case 17: read_slot<17>(a0, a1, a4, pk); break;
+    case 18: read_slot<18>(a0, a1, a4, pk); break;
+    case 19: read_slot<19>(a0, a1, a4, pk); break;
+    case 20: read_slot<20>(a0, a1, a4, pk); break;
+    case 21: read_slot<21>(a0, a1, a4, pk); break;
+    case 22: read_slot<22>(a0, a1, a4, pk); break;
+    case 23: read_slot<23>(a0, a1, a4, pk); break;
+    case 24: read_slot<24>(a0, a1, a4, pk); break;
+    case 25: read_slot<25>(a0, a1, a4, pk); break;
+    case 26: read_slot<26>(a0, a1, a4, pk); break;
+    case 27: read_slot<27>(a0, a1, a4, pk); break;
+    case 28: read_slot<28>(a0, a1, a4, pk); break;
+    case 29: read_slot<29>(a0, a1, a4, pk); break;
+    case 30: read_slot<30>(a0, a1, a4, pk); break;
+    case 31: read_slot<31>(a0, a1, a4, pk); break;
+    default: read_slot<0>(a0, a1, a4, pk); break;
+  }
+}
+
+// -inf fill work of one wave: its share [a, z) of the row-major (row, page
+// slot) grid, of which only slots past each row's live pages are written.
+struct FillCursor {
+  int64_t a, z;          // share not yet scanned
+  int32_t r, j, jend;    // current row r: dead pages [j, jend) still to write
+};
+
+__device__ __forceinline__ FillCursor fill_cursor(const Params& p, int64_t wid, int64_t nw) {
+  const int64_t slots = (int64_t)p.rows * p.width;
+  FillCursor fc;
+  fc.a = uniform(wid * slots / nw);
+  fc.z = uniform((wid + 1) * slots / nw);
+  fc.r = 0;
+  fc.j = 0;
+  fc.jend = 0;
+  return fc;
+}
+
+__device__ __forceinline__ bool fill_next_segment(const Params& p, FillCursor& fc) {
+  const int32_t width = p.width;
+  while (fc.a < fc.z) {
+    const int32_t r = uniform((int32_t)(fc.a / width)), j = uniform((int32_t)(fc.a % width));
+    const int32_t jend = uniform((int32_t)min<int64_t>(width, j + (fc.z - fc.a)));
+    const int32_t d0 = max(j, live_pages_of(clamp_len(load_uniform(p.sl, r), width)));
+    fc.a = uniform(fc.a + (jend - j));
+    if (d0 < jend) {
+      fc.r = r;
+      fc.j = uniform(d0);
+      fc.jend = jend;
+      return true;
+    }
+  }
+  return false;
+}
+
+__device__ __forceinline__ void fill_rest(const Params& p, FillCursor& fc, int lane) {
+  do {
+    if (fc.j < fc.jend) {
+      fill_neg_inf(p.out + (int64_t)fc.r * p.width * kPage, fc.j, fc.jend - fc.j, lane);
+      fc.j = fc.jend;
+    }
+  } while (fill_next_segment(p, fc));
+}
+
+// Live pages [ja, jb) of row b through the wave's NS LDS slots: NS pages are
+// in flight while one is multiplied.
+template <int NS>
+__device__ __forceinline__ void row_pages_dma(const Params& p, int32_t b, int32_t ja, int32_t jb,
+                                              int32_t L, int lane, lds_u8* slots) {
+  RowQuery rq;
+  load_row_query(p, b, lane, rq);
+  const int32_t* tab = p.pt + (int64_t)b * p.pt_stride;
+  float* orow = p.out + (int64_t)b * p.width * kPage;
+  // A page id outside the pool is never dereferenced: its DMA reads the row's
+  // own query bytes instead (always valid memory) and its logits become NaN.
+  const uint8_t* safe = p.q + (int64_t)b * (kHeads * kDim * 2);
+  const int32_t J = jb - ja;
+  bool ok[NS];
+#pragma unroll
+  for (int t = 0; t < NS; ++t) {
+    // (a short segment still issues NS groups, the extra ones from the query
+    // row, so that the prologue always holds NS groups)
+    const int32_t g = t < J ? load_uniform(tab, ja + t) : -1;
+    ok[t] = page_ok(g, p.num_pages);
+    const uint8_t* keys = ok[t] ? p.kv + (int64_t)g * p.kv_stride : safe;
+    const uint8_t* sc = ok[t] ? p.ks + (int64_t)g * p.ks_stride : safe + 8192;
+    dma_page(keys, sc, slots + t * kSlotBytes, lane);
+  }
+  // The query and weights were requested before the NS DMA groups (9
+  // operations each): wait for them here with the groups still in flight, so
+  // that no conservative wait for them lands inside the page loop.
+  __builtin_amdgcn_s_waitcnt(wait_vm(kDmaOps * NS));
+  const uint32_t base = (uint32_t)(uintptr_t)slots;
+  const uint32_t off0 = slot_chunk_offset(lane, 0), off1 = slot_chunk_offset(lane, 1);
+  // page id of the group issued next; read one iteration ahead so the scalar
+  // load never stalls the DMA issue
+  int32_t g_ahead = (NS < J) ? load_uniform(tab, ja + NS) : -1;
+  for (int32_t t = 0; t < J; t += NS) {
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const int32_t tt = t + u;
+      if (tt < J) {
+        lds_u8* slot = slots + u * kSlotBytes;
+        const uint32_t a0 = base + u * kSlotBytes + off0;
+        const uint32_t a1 = base + u * kSlotBytes + off1;
+        const uint32_t a4 = base + u * kSlotBytes + 8192 + 4 * lane;
+        // Operations issued after page tt's DMA group: one store per earlier
+        // iteration since that group (min(tt, NS) of them) and the groups of
+        // the pages after it -- prologue groups for tt < NS, plus one group
+        // per iteration i in [tt-NS+1, tt-1] with i+NS < J.
+        const int32_t lo = max(0, tt - NS + 1), hi = min(tt - 1, J - NS - 1);
+        const int32_t groups = (tt < NS ? NS - 1 - tt : 0) + max(0, hi - lo + 1);
+        const int32_t n_after = min(tt, NS) + kDmaOps * groups;
+        PageKeys<kFp8> pk;
+        read_slot_after(uniform(n_after), a0, a1, a4, pk);
+        const bool cur_ok = ok[u];
+        const int32_t g = g_ahead;
+        g_ahead = (tt + NS + 1 < J) ? load_uniform(tab, ja + tt + NS + 1) : -1;
+        if (tt + NS < J) {
+          ok[u] = page_ok(g, p.num_pages);
+          const uint8_t* keys = ok[u] ? p.kv + (int64_t)g * p.kv_stride : safe;
+          const uint8_t* sc = ok[u] ? p.ks + (int64_t)g * p.ks_stride : safe + 8192;
+          dma_page(keys, sc, slot, lane);
+        }
+        if (cur_ok)
+          store_page(orow, ja + tt, L, lane, score_page<kFp8>(rq, pk, lane));
+        else
+          store_bad_page(orow, ja + tt, L, lane);
+      }
+    }
+  }
+}
+
+// Live pages [s, e) of the row-major sequence of all rows' live pages.
+template <int KEY, int NS>
+__device__ __forceinline__ void live_share(const Params& p, int64_t s, int64_t e, int lane,
+                                           lds_u8* my_slots) {
+  const int32_t rows = p.rows, width = p.width;
+
+  // Row holding live page s and the number of live pages before that row.
+  int32_t r = 0;
+  int64_t excl = 0;
+  for (int32_t r0 = 0; r0 < rows; r0 += 64) {
+    const int32_t rr = r0 + lane;
+    const int32_t lp = rr < rows ? live_pages_of(clamp_len(p.sl[rr], width)) : 0;
+    const int32_t incl = wave_inclusive_scan(lp, lane);
+    const int32_t csum = __builtin_amdgcn_readlane(incl, 63);
+    if (excl + csum > s) {
+      const uint64_t m = __ballot(excl + incl > s);
+      const int first = uniform((int32_t)__builtin_ctzll(m));
+      r = uniform(r0 + first);
+      excl = uniform(excl + __builtin_amdgcn_readlane(incl - lp, first));
+      break;
+    }
+    excl = uniform(excl + csum);
+  }
+
+  int64_t pos = s;
+  while (pos < e) {
+    const int32_t L = clamp_len(load_uniform(p.sl, r), width);
+    const int32_t lp = live_pages_of(L);
+    const int32_t ja = (int32_t)(pos - excl);
+    const int32_t jb = (int32_t)min<int64_t>(lp, e - excl);
+    if (ja < jb) {
+      if constexpr (KEY == kFp8)
+        row_pages_dma<NS>(p, r, ja, jb, L, lane, my_slots);
+      else
+        row_pages<KEY, 2>(p, r, ja, jb, L, lane);
+    }
+    pos = uniform(excl + jb);
+    excl = uniform(excl + lp);
+    r = uniform(r + 1);
+  }
+}
+
+template <int KEY, int WAVES, int NS>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(KEY == kFp8 ? 2 : 1, 2))) void balanced_kernel(Params p) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t nw = (int64_t)gridDim.x * WAVES;
+  const int64_t wid = (int64_t)blockIdx.x * WAVES + wave;
+  const int32_t rows = p.rows, width = p.width;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[(KEY == kFp8) ? WAVES * NS * kSlotBytes : 16];
+  lds_u8* dma_slots = (lds_u8*)lds_raw;
+
+  // (1) total live pages, then this wave's range [s, e) of them.
+  int64_t acc = 0;
+  for (int32_t r0 = 0; r0 < rows; r0 += 64) {
+    const int32_t r = r0 + lane;
+    if (r < rows) acc += live_pages_of(clamp_len(p.sl[r], width));
+  }
+  const int64_t total = uniform(wave_sum(acc));
+  const int64_t s = wid * total / nw, e = (wid + 1) * total / nw;
+  // (2) the -inf share rides along with the live pages (fp8) and whatever is
+  // left is written at the end.
+  // Workgroups of the grid's second half score first and write -inf after,
+  // those of the first half the reverse.  The dispatcher gives every CU one
+  // workgroup of each half, so each SIMD keeps one wave on the MFMA/VALU-heavy
+  // scoring while the other streams stores, and HBM sees reads and writes
+  // together.
+  FillCursor fc = fill_cursor(p, wid, nw);
+  if (2 * blockIdx.x >= gridDim.x) {
+    if (s < e) live_share<KEY, NS>(p, s, e, lane, dma_slots + wave * NS * kSlotBytes);
+    fill_rest(p, fc, lane);
+  } else {
+    fill_rest(p, fc, lane);
+    if (s < e) live_share<KEY, NS>(p, s, e, lane, dma_slots + wave * NS * kSlotBytes);
   }
 }
 
@@ -308,11 +742,11 @@ __device__ __forceinline__ void load_page_lds(const uint8_t* lds, int lane, Page
 #pragma unroll
     for (int v = 0; v < kVec; ++v)
       pk.v[nb][v] = *reinterpret_cast<const u32x4*>(lds + LdsPage<KEY>::chunk_off(i, kVec * g + v));
-    if constexpr (KEY == kFp8)
-      pk.s[nb] = reinterpret_cast<const float*>(lds + LdsPage<KEY>::kKeyBytes)[i];
-    else
-      pk.s[nb] = 1.0f;
   }
+  if constexpr (KEY == kFp8)
+    pk.s = reinterpret_cast<const float*>(lds + LdsPage<KEY>::kKeyBytes)[lane];
+  else
+    pk.s = 1.0f;
 }
 
 template <int KEY, int CHUNK>
@@ -349,9 +783,9 @@ __global__ __launch_bounds__(64 * kSharedRows) void shared_kernel(Params p, int3
 #pragma unroll
     for (int r = 0; r < kSharedRows; ++r) {
       const int32_t br = rb * kSharedRows + r;
-      if (br < p.rows) Lmax = max(Lmax, clamp_len(p.sl[br], width));
+      if (br < p.rows) Lmax = max(Lmax, clamp_len(load_uniform(p.sl, br), width));
     }
-    const int32_t L = row_ok ? clamp_len(p.sl[b], width) : 0;
+    const int32_t L = row_ok ? clamp_len(load_uniform(p.sl, b), width) : 0;
     const int32_t live_w = (L + kPage - 1) / kPage;
     const int32_t jl = max(j0, min(jend, (Lmax + kPage - 1) / kPage));  // pages any row needs
 
@@ -359,7 +793,7 @@ __global__ __launch_bounds__(64 * kSharedRows) void shared_kernel(Params p, int3
       RowQuery rq;
       if (row_ok && j0 < live_w) load_row_query(p, b, lane, rq);
       Stage<KEY> st;
-      int32_t gcur = tab[j0];
+      int32_t gcur = load_uniform(tab, j0);
       bool okcur = page_ok(gcur, p.num_pages);
       if (okcur) stage_load<KEY>(p, gcur, tid, st);
       for (int32_t j = j0; j < jl; ++j) {
@@ -369,7 +803,7 @@ __global__ __launch_bounds__(64 * kSharedRows) void shared_kernel(Params p, int3
         int32_t gnxt = 0;
         bool oknxt = false;
         if (j + 1 < jl) {
-          gnxt = tab[j + 1];
+          gnxt = load_uniform(tab, j + 1);
           oknxt = page_ok(gnxt, p.num_pages);
           if (oknxt) stage_load<KEY>(p, gnxt, tid, st);
         }
@@ -401,6 +835,24 @@ constexpr int kRowwiseWaves = 4;
 constexpr int kSharedChunk = 8;
 constexpr int64_t kMaxGrid = (int64_t)1 << 20;  // larger grids loop (grid-stride)
 constexpr int32_t kMaxWidth = 1 << 24;
+
+constexpr int kBalancedWaves = 4;
+constexpr int kBalancedWgPerCu = 2;
+constexpr int kBalancedSlots = 2;  // fp8 pages in flight per wave (LDS slots)
+
+// Compute units of the current device (queried once per device).
+int device_cu_count() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
 
 inline bool aligned(const void* ptr, uintptr_t a) { return ((uintptr_t)ptr & (a - 1)) == 0; }
 
@@ -454,6 +906,17 @@ int launch(const void* q, const void* kv_pages, const float* kscale, const int32
   p.width = table_width;
 
   (void)hipGetLastError();  // start from a clean error state
+  if (page_table_row_stride != 0 || rows == 1) {
+    if (rows <= kBalancedMaxRows) {
+      const int64_t slots = (int64_t)rows * table_width;
+      const int64_t want = (slots + 7) / 8;
+      const int64_t cap = (int64_t)kBalancedWgPerCu * device_cu_count();
+      const int64_t grid = want < 1 ? 1 : (want < cap ? want : cap);
+      balanced_kernel<KEY, kBalancedWaves, kBalancedSlots>
+          <<<dim3((uint32_t)grid), dim3(64 * kBalancedWaves), 0, stream>>>(p);
+      return hipGetLastError() == hipSuccess ? IDX_OK : IDX_ERR_LAUNCH;
+    }
+  }
   if (page_table_row_stride == 0 && rows > 1) {
     const int32_t row_blocks = (rows + kSharedRows - 1) / kSharedRows;
     const int32_t chunks = (table_width + kSharedChunk - 1) / kSharedChunk;
