@@ -683,7 +683,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(KEY 
 
 // ---------------------------------------------------------------------------
 // shared kernel: rows share one page table.  Unit = (block of 4 rows, chunk of
-// CHUNK page slots); wave w scores row 4*rb + w.  Pages go through LDS.
+// `chunk` page slots); wave w scores row 4*rb + w.  Pages go through LDS.
 constexpr int kSharedRows = 4;
 
 template <int KEY>
@@ -749,9 +749,10 @@ __device__ __forceinline__ void load_page_lds(const uint8_t* lds, int lane, Page
     pk.s = 1.0f;
 }
 
-template <int KEY, int CHUNK>
+template <int KEY>
 __global__ __launch_bounds__(64 * kSharedRows) void shared_kernel(Params p, int32_t row_blocks,
-                                                                  int32_t chunks, int32_t rb_per_xcd,
+                                                                  int32_t chunk, int32_t chunks,
+                                                                  int32_t rb_per_xcd,
                                                                   int64_t total_slots) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][LdsPage<KEY>::kBytes];
   const int tid = threadIdx.x;
@@ -772,8 +773,8 @@ __global__ __launch_bounds__(64 * kSharedRows) void shared_kernel(Params p, int3
     if (rb_local >= rb_per_xcd || rb_rev >= row_blocks) continue;
     const int32_t rb = row_blocks - 1 - rb_rev;
 
-    const int32_t j0 = c * CHUNK;
-    const int32_t jend = min(j0 + CHUNK, width);
+    const int32_t j0 = c * chunk;
+    const int32_t jend = min(j0 + chunk, width);
     const int32_t b = rb * kSharedRows + wave;
     const bool row_ok = b < p.rows;
     float* orow = p.out + (int64_t)b * width * kPage;
@@ -832,7 +833,7 @@ __global__ __launch_bounds__(64 * kSharedRows) void shared_kernel(Params p, int3
 
 constexpr int kRowwisePPW = 2;
 constexpr int kRowwiseWaves = 4;
-constexpr int kSharedChunk = 8;
+constexpr int kSharedTargetWgPerCu = 4;  // units per CU wanted before splitting rows into chunks
 constexpr int64_t kMaxGrid = (int64_t)1 << 20;  // larger grids loop (grid-stride)
 constexpr int32_t kMaxWidth = 1 << 24;
 
@@ -919,12 +920,18 @@ int launch(const void* q, const void* kv_pages, const float* kscale, const int32
   }
   if (page_table_row_stride == 0 && rows > 1) {
     const int32_t row_blocks = (rows + kSharedRows - 1) / kSharedRows;
-    const int32_t chunks = (table_width + kSharedChunk - 1) / kSharedChunk;
+    // Whole rows per unit (the query is read once) unless that leaves too few
+    // units to fill the chip; then split the table into chunks.
+    const int64_t want = (int64_t)kSharedTargetWgPerCu * device_cu_count();
+    int32_t chunks = (int32_t)((want + row_blocks - 1) / row_blocks);
+    chunks = chunks < 1 ? 1 : (chunks > table_width ? table_width : chunks);
+    const int32_t chunk = (table_width + chunks - 1) / chunks;
+    chunks = (table_width + chunk - 1) / chunk;
     const int32_t rb_per_xcd = (row_blocks + 7) / 8;
     const int64_t total = (int64_t)8 * rb_per_xcd * chunks;
     const int64_t grid = total < kMaxGrid ? total : kMaxGrid;
-    shared_kernel<KEY, kSharedChunk><<<dim3((uint32_t)grid), dim3(64 * kSharedRows), 0, stream>>>(
-        p, row_blocks, chunks, rb_per_xcd, total);
+    shared_kernel<KEY><<<dim3((uint32_t)grid), dim3(64 * kSharedRows), 0, stream>>>(
+        p, row_blocks, chunk, chunks, rb_per_xcd, total);
   } else {
     constexpr int per_unit = kRowwisePPW * kRowwiseWaves;
     const int32_t units_per_row = (table_width + per_unit - 1) / per_unit;
