@@ -163,6 +163,24 @@ __device__ __forceinline__ float block_epilogue(const RowQuery& rq, const f32x4 
   return sum;
 }
 
+// part[nb] of lane (g, n) -> sum over g of part[g] of lanes (., n), in lane (g, n).
+// permlane16_swap(x, y) trades rows 1, 3 of x with rows 0, 2 of y (a row is 16
+// lanes), so x' + y' holds, per row pair {0,1} / {2,3}, the pair sums of x
+// (rows 0 and 2) and of y (rows 1 and 3); permlane32_swap then trades the upper
+// half of one such sum with the lower half of the other.
+__device__ __forceinline__ float reduce_heads(const float (&part)[4]) {
+  // (elements of the returned pairs go through __uint_as_float: a bit_cast of
+  // an ext-vector element is folded to element 0 by this compiler)
+  const auto s01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(part[0]), __float_as_uint(part[1]),
+                                                    false, false);
+  const auto s23 = __builtin_amdgcn_permlane16_swap(__float_as_uint(part[2]), __float_as_uint(part[3]),
+                                                    false, false);
+  const float t = __uint_as_float(s01[0]) + __uint_as_float(s01[1]);
+  const float u = __uint_as_float(s23[0]) + __uint_as_float(s23[1]);
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(u), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
 // Score one page: returns the logit of position 64*j + lane (before masking).
 //   x[h][i]  = <q[h], k_i>                       (MFMA, fp32 accumulate)
 //   logit_i  = |s_i| * sum_h w[h] * ReLU(x')      with x' = x for s_i >= 0 and
@@ -203,15 +221,7 @@ __device__ __forceinline__ float score_page_impl(const RowQuery& rq, const PageK
     }
   }
   part[3] = block_epilogue(rq, acc[1]);
-  // step 1 (partner g^1): keep blocks nb with nb%2 == g%2, send the others
-  const bool b0 = g & 1, b1 = g & 2;
-  const float keep0 = b0 ? part[1] : part[0], keep1 = b0 ? part[3] : part[2];
-  const float send0 = b0 ? part[0] : part[1], send1 = b0 ? part[2] : part[3];
-  const float t0 = keep0 + __shfl_xor(send0, 16);  // block g%2
-  const float t1 = keep1 + __shfl_xor(send1, 16);  // block g%2 + 2
-  // step 2 (partner g^2): keep block g
-  const float keep = b1 ? t1 : t0, send = b1 ? t0 : t1;
-  const float total = keep + __shfl_xor(send, 32);
+  const float total = reduce_heads(part);
   return (KEY == kFp8) ? fabsf(pk.s) * total : total;
 }
 
