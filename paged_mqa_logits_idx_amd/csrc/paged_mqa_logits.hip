@@ -709,65 +709,139 @@ struct LdsPage {
   }
 };
 
-// Per-thread share of one page copy: 16-byte chunks (plus scale chunks).
+// One page of the shared table through LDS by DMA: wave w copies its quarter
+// of the key rows (16 B per lane, the XOR swizzle of LdsPage applied on the
+// source side since the DMA destination is lane-linear); wave 0 also copies
+// the 256 scale bytes (fp8).  Returns nothing; the wave's operation count per
+// page is kSharedDmaOps(w).
 template <int KEY>
-struct Stage {
-  static constexpr int kKeyChunks = LdsPage<KEY>::kKeyBytes / 16 / (64 * kSharedRows);  // 2 / 4
-  u32x4 v[kKeyChunks];
-  u32x4 sc;  // threads 0..15 carry the 256 scale bytes (fp8)
-};
-
-template <int KEY>
-__device__ __forceinline__ void stage_load(const Params& p, int32_t gp, int tid, Stage<KEY>& st) {
-  const uint8_t* base = p.kv + (int64_t)gp * p.kv_stride;
+__device__ __forceinline__ void shared_dma_page(const uint8_t* page, const uint8_t* scales, lds_u8* slot,
+                                                int wave, int lane) {
+  if constexpr (KEY == kBf16) {
+    // 16 rows of 256 B per wave: 4 DMAs of 4 rows each
 #pragma unroll
-  for (int c = 0; c < Stage<KEY>::kKeyChunks; ++c)
-    st.v[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base) + tid + c * 64 * kSharedRows);
-  if constexpr (KEY == kFp8) {
-    if (tid < 16)
-      st.sc = *reinterpret_cast<const u32x4*>(p.ks + (int64_t)gp * p.ks_stride + 16 * tid);
+    for (int t = 0; t < 4; ++t) {
+      const int i = 16 * wave + 4 * t + (lane >> 4), c = lane & 15;
+      __builtin_amdgcn_global_load_lds((global_ptr)(page + i * 256 + 16 * (c ^ (i & 15))),
+                                       (lds_ptr)(slot + (16 * wave + 4 * t) * 256), 16, 0, 0);
+    }
+  } else {
+    // 16 rows of 128 B per wave: 2 DMAs of 8 rows each
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int i = 16 * wave + 8 * t + (lane >> 3), c = lane & 7;
+      __builtin_amdgcn_global_load_lds((global_ptr)(page + i * 128 + 16 * (c ^ (i & 7))),
+                                       (lds_ptr)(slot + (16 * wave + 8 * t) * 128), 16, 0, 0);
+    }
+    if (wave == 0)
+      __builtin_amdgcn_global_load_lds((global_ptr)(scales + 4 * lane), (lds_ptr)(slot + 8192), 4, 0, 0);
   }
 }
 
-template <int KEY>
-__device__ __forceinline__ void stage_store(uint8_t* lds, int tid, const Stage<KEY>& st) {
-  constexpr int kChunks = LdsPage<KEY>::kChunks;
-#pragma unroll
-  for (int c = 0; c < Stage<KEY>::kKeyChunks; ++c) {
-    const int ci = tid + c * 64 * kSharedRows;
-    *reinterpret_cast<u32x4*>(lds + LdsPage<KEY>::chunk_off(ci / kChunks, ci % kChunks)) = st.v[c];
-  }
-  if constexpr (KEY == kFp8) {
-    if (tid < 16) *reinterpret_cast<u32x4*>(lds + LdsPage<KEY>::kKeyBytes + 16 * tid) = st.sc;
-  }
-}
-
-template <int KEY>
-__device__ __forceinline__ void load_page_lds(const uint8_t* lds, int lane, PageKeys<KEY>& pk) {
+// bf16 page from its LDS slot into the lane's B fragments (layout of LdsPage):
+// lane (g, n) reads chunks 4g .. 4g+3 of rows n, 16+n, 32+n, 48+n.  Waits
+// until at most N vector-memory operations are outstanding first (the
+// compiler does not see these reads, so it adds no wait for the DMAs still in
+// flight into other slots).
+template <int N>
+__device__ __forceinline__ void read_slot_bf16(uint32_t sb, int lane, PageKeys<kBf16>& pk) {
   const int n = lane & 15, g = lane >> 4;
-  constexpr int kVec = PageKeys<KEY>::kVec;
+  uint32_t a[4];
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const int i = 16 * nb + n;
-#pragma unroll
-    for (int v = 0; v < kVec; ++v)
-      pk.v[nb][v] = *reinterpret_cast<const u32x4*>(lds + LdsPage<KEY>::chunk_off(i, kVec * g + v));
-  }
-  if constexpr (KEY == kFp8)
-    pk.s = reinterpret_cast<const float*>(lds + LdsPage<KEY>::kKeyBytes)[lane];
-  else
-    pk.s = 1.0f;
+  for (int v = 0; v < 4; ++v) a[v] = sb + (uint32_t)(n * 256 + 16 * ((4 * g + v) ^ n));
+  asm volatile(
+      "s_waitcnt vmcnt(%20)\n\t"
+      "ds_read_b128 %0, %16\n\t"
+      "ds_read_b128 %1, %17\n\t"
+      "ds_read_b128 %2, %18\n\t"
+      "ds_read_b128 %3, %19\n\t"
+      "ds_read_b128 %4, %16 offset:4096\n\t"
+      "ds_read_b128 %5, %17 offset:4096\n\t"
+      "ds_read_b128 %6, %18 offset:4096\n\t"
+      "ds_read_b128 %7, %19 offset:4096\n\t"
+      "ds_read_b128 %8, %16 offset:8192\n\t"
+      "ds_read_b128 %9, %17 offset:8192\n\t"
+      "ds_read_b128 %10, %18 offset:8192\n\t"
+      "ds_read_b128 %11, %19 offset:8192\n\t"
+      "ds_read_b128 %12, %16 offset:12288\n\t"
+      "ds_read_b128 %13, %17 offset:12288\n\t"
+      "ds_read_b128 %14, %18 offset:12288\n\t"
+      "ds_read_b128 %15, %19 offset:12288\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(pk.v[0][0]), "=&v"(pk.v[0][1]), "=&v"(pk.v[0][2]), "=&v"(pk.v[0][3]),
+        "=&v"(pk.v[1][0]), "=&v"(pk.v[1][1]), "=&v"(pk.v[1][2]), "=&v"(pk.v[1][3]),
+        "=&v"(pk.v[2][0]), "=&v"(pk.v[2][1]), "=&v"(pk.v[2][2]), "=&v"(pk.v[2][3]),
+        "=&v"(pk.v[3][0]), "=&v"(pk.v[3][1]), "=&v"(pk.v[3][2]), "=&v"(pk.v[3][3])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "n"(N)
+      : "memory");
+  pk.s = 1.0f;
 }
+
+// Wait until at most n (<= 11) vector-memory operations are outstanding.
+__device__ __forceinline__ void wait_vm_n(int32_t n) {
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(wait_vm(0)); break;
+    case 1: __builtin_amdgcn_s_waitcnt(wait_vm(1)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(wait_vm(2)); break;
+    case 3: __builtin_amdgcn_s_waitcnt(wait_vm(3)); break;
+    case 4: __builtin_amdgcn_s_waitcnt(wait_vm(4)); break;
+    case 5: __builtin_amdgcn_s_waitcnt(wait_vm(5)); break;
+    case 6: __builtin_amdgcn_s_waitcnt(wait_vm(6)); break;
+    case 7: __builtin_amdgcn_s_waitcnt(wait_vm(7)); break;
+    case 8: __builtin_amdgcn_s_waitcnt(wait_vm(8)); break;
+    case 9: __builtin_amdgcn_s_waitcnt(wait_vm(9)); break;
+    case 10: __builtin_amdgcn_s_waitcnt(wait_vm(10)); break;
+    case 11: __builtin_amdgcn_s_waitcnt(wait_vm(11)); break;
+    default: __builtin_amdgcn_s_waitcnt(wait_vm(0)); break;
+  }
+}
+
+// Page of a slot after waiting until n operations remain outstanding.
+template <int KEY>
+__device__ __forceinline__ void read_shared_slot(int32_t n, uint32_t sb, int lane, PageKeys<KEY>& pk) {
+  if constexpr (KEY == kBf16) {
+    switch (n) {
+      case 0: read_slot_bf16<0>(sb, lane, pk); break;
+      case 1: read_slot_bf16<1>(sb, lane, pk); break;
+      case 2: read_slot_bf16<2>(sb, lane, pk); break;
+      case 3: read_slot_bf16<3>(sb, lane, pk); break;
+      case 4: read_slot_bf16<4>(sb, lane, pk); break;
+      case 5: read_slot_bf16<5>(sb, lane, pk); break;
+      case 6: read_slot_bf16<6>(sb, lane, pk); break;
+      case 7: read_slot_bf16<7>(sb, lane, pk); break;
+      case 8: read_slot_bf16<8>(sb, lane, pk); break;
+      case 9: read_slot_bf16<9>(sb, lane, pk); break;
+      case 10: read_slot_bf16<10>(sb, lane, pk); break;
+      case 11: read_slot_bf16<11>(sb, lane, pk); break;
+      default: read_slot_bf16<0>(sb, lane, pk); break;
+    }
+  } else {
+    const uint32_t a0 = sb + slot_chunk_offset(lane, 0), a1 = sb + slot_chunk_offset(lane, 1);
+    read_slot_after(n, a0, a1, sb + 8192 + 4 * lane, pk);
+  }
+}
+
+// Rows sharing one page table (page_table_row_stride == 0: the query tokens of
+// one prefill request).  Unit = (block of 4 rows, chunk of `chunk` page
+// slots); wave w scores row 4*rb + w.  Each page is copied once into LDS by
+// DMA -- kSharedSlots slots, pages kSharedSlots-1 ahead in flight -- and all 4
+// waves multiply it against their own row's query; one barrier per page.
+constexpr int kSharedSlots = 3;
 
 template <int KEY>
 __global__ __launch_bounds__(64 * kSharedRows) void shared_kernel(Params p, int32_t row_blocks,
                                                                   int32_t chunk, int32_t chunks,
                                                                   int32_t rb_per_xcd,
                                                                   int64_t total_slots) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][LdsPage<KEY>::kBytes];
+  constexpr int NS = kSharedSlots;
+  constexpr int kSlot = (KEY == kFp8) ? kSlotBytes : 16384;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[NS * kSlot];
+  lds_u8* slots = (lds_u8*)lds_raw;
+  const uint32_t base = (uint32_t)(uintptr_t)slots;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int32_t ops = (KEY == kFp8) ? (wave == 0 ? 3 : 2) : 4;  // DMA operations per page
   const int32_t width = p.width;
   const int32_t* tab = p.pt;  // shared table (row stride 0)
 
@@ -803,36 +877,57 @@ __global__ __launch_bounds__(64 * kSharedRows) void shared_kernel(Params p, int3
     if (j0 < jl) {
       RowQuery rq;
       if (row_ok && j0 < live_w) load_row_query(p, b, lane, rq);
-      Stage<KEY> st;
-      int32_t gcur = load_uniform(tab, j0);
-      bool okcur = page_ok(gcur, p.num_pages);
-      if (okcur) stage_load<KEY>(p, gcur, tid, st);
-      for (int32_t j = j0; j < jl; ++j) {
-        uint8_t* buf = lds[(j - j0) & 1];
-        if (okcur) stage_store<KEY>(buf, tid, st);
-        __syncthreads();
-        int32_t gnxt = 0;
-        bool oknxt = false;
-        if (j + 1 < jl) {
-          gnxt = load_uniform(tab, j + 1);
-          oknxt = page_ok(gnxt, p.num_pages);
-          if (oknxt) stage_load<KEY>(p, gnxt, tid, st);
-        }
+      // A page id outside the pool -- or a page past jl, issued only to keep
+      // the operation count per iteration constant -- is copied from the
+      // query buffer instead (always valid memory, at least 16 KiB).
+      uint32_t ok_bits = 0;  // bit t % NS: page j0 + t has a valid id
+      auto issue = [&](int32_t t) {
+        const int32_t j = j0 + t;
+        const int32_t g = j < jl ? load_uniform(tab, j) : -1;
+        const bool ok = page_ok(g, p.num_pages);
+        const int u = t % NS;
+        ok_bits = (uint32_t)uniform((int32_t)((ok_bits & ~(1u << u)) | ((ok ? 1u : 0u) << u)));
+        const uint8_t* page = ok ? p.kv + (int64_t)g * p.kv_stride : p.q;
+        const uint8_t* sc = (KEY == kFp8 && ok) ? p.ks + (int64_t)g * p.ks_stride : p.q + 8192;
+        shared_dma_page<KEY>(page, sc, slots + u * kSlot, wave, lane);
+      };
+#pragma unroll
+      for (int t = 0; t < NS - 1; ++t) issue(t);
+      // The query was requested before these DMAs: wait for it here with them
+      // still in flight, so that no conservative wait lands in the page loop.
+      // (Wave 0 of the fp8 kernel has one more operation per page; waiting on
+      // the smaller count there costs it a part of page 0, no more.)
+      __builtin_amdgcn_s_waitcnt(wait_vm((NS - 1) * ((KEY == kFp8) ? 2 : 4)));
+      const int32_t st = row_ok ? 1 : 0;  // stores per iteration
+      for (int32_t t = 0; j0 + t < jl; ++t) {
+        const int32_t j = j0 + t;
+        const int u = t % NS;
+        // Operations issued after page t's DMA: the pages of the (NS-2) later
+        // DMAs and the stores of the min(t, NS-1) iterations since it.
+        const int32_t n_after = uniform(min(t, NS - 1) * st + (NS - 2) * ops);
+        PageKeys<KEY> pk;
+        const bool need = row_ok && j < live_w;
+        // Every wave waits for its own part of page t, then the barrier makes
+        // the whole page visible -- and also guarantees that every wave is
+        // done with slot (t-1) % NS, which the next DMA overwrites.
+        if (need)
+          read_shared_slot<KEY>(n_after, base + (uint32_t)(u * kSlot), lane, pk);
+        else
+          wait_vm_n(n_after);
+        __builtin_amdgcn_s_barrier();
+        issue(t + NS - 1);
         if (row_ok) {
           if (j >= live_w) {
             store_page(orow, j, 0, lane, 0.f);  // whole page past this row's length
-          } else if (okcur) {
-            PageKeys<KEY> pk;
-            load_page_lds<KEY>(buf, lane, pk);
+          } else if ((ok_bits >> u) & 1u) {
             store_page(orow, j, L, lane, score_page<KEY>(rq, pk, lane));
           } else {
             store_bad_page(orow, j, L, lane);
           }
         }
-        okcur = oknxt;
-        gcur = gnxt;
       }
-      __syncthreads();  // LDS is reused by this workgroup's next slot
+      __builtin_amdgcn_s_waitcnt(wait_vm(0));
+      __builtin_amdgcn_s_barrier();  // LDS is reused by this workgroup's next unit
     }
     if (row_ok && jl < jend) fill_neg_inf(orow, jl, jend - jl, lane);
   }
