@@ -796,28 +796,14 @@ __device__ __forceinline__ void wait_vm_n(int32_t n) {
   }
 }
 
-// Page of a slot after waiting until n operations remain outstanding.
+// Page of a slot whose DMA is known complete (the wait count 63 is no wait).
 template <int KEY>
-__device__ __forceinline__ void read_shared_slot(int32_t n, uint32_t sb, int lane, PageKeys<KEY>& pk) {
+__device__ __forceinline__ void read_shared_slot(uint32_t sb, int lane, PageKeys<KEY>& pk) {
   if constexpr (KEY == kBf16) {
-    switch (n) {
-      case 0: read_slot_bf16<0>(sb, lane, pk); break;
-      case 1: read_slot_bf16<1>(sb, lane, pk); break;
-      case 2: read_slot_bf16<2>(sb, lane, pk); break;
-      case 3: read_slot_bf16<3>(sb, lane, pk); break;
-      case 4: read_slot_bf16<4>(sb, lane, pk); break;
-      case 5: read_slot_bf16<5>(sb, lane, pk); break;
-      case 6: read_slot_bf16<6>(sb, lane, pk); break;
-      case 7: read_slot_bf16<7>(sb, lane, pk); break;
-      case 8: read_slot_bf16<8>(sb, lane, pk); break;
-      case 9: read_slot_bf16<9>(sb, lane, pk); break;
-      case 10: read_slot_bf16<10>(sb, lane, pk); break;
-      case 11: read_slot_bf16<11>(sb, lane, pk); break;
-      default: read_slot_bf16<0>(sb, lane, pk); break;
-    }
+    read_slot_bf16<63>(sb, lane, pk);
   } else {
     const uint32_t a0 = sb + slot_chunk_offset(lane, 0), a1 = sb + slot_chunk_offset(lane, 1);
-    read_slot_after(n, a0, a1, sb + 8192 + 4 * lane, pk);
+    read_slot<63>(a0, a1, sb + 8192 + 4 * lane, pk);
   }
 }
 
@@ -826,7 +812,7 @@ __device__ __forceinline__ void read_shared_slot(int32_t n, uint32_t sb, int lan
 // slots); wave w scores row 4*rb + w.  Each page is copied once into LDS by
 // DMA -- kSharedSlots slots, pages kSharedSlots-1 ahead in flight -- and all 4
 // waves multiply it against their own row's query; one barrier per page.
-constexpr int kSharedSlots = 3;
+constexpr int kSharedSlots = 2;
 
 template <int KEY>
 __global__ __launch_bounds__(64 * kSharedRows) void shared_kernel(Params p, int32_t row_blocks,
@@ -905,16 +891,13 @@ __global__ __launch_bounds__(64 * kSharedRows) void shared_kernel(Params p, int3
         // Operations issued after page t's DMA: the pages of the (NS-2) later
         // DMAs and the stores of the min(t, NS-1) iterations since it.
         const int32_t n_after = uniform(min(t, NS - 1) * st + (NS - 2) * ops);
-        PageKeys<KEY> pk;
-        const bool need = row_ok && j < live_w;
-        // Every wave waits for its own part of page t, then the barrier makes
+        // Every wave waits for its own part of page t; the barrier then makes
         // the whole page visible -- and also guarantees that every wave is
         // done with slot (t-1) % NS, which the next DMA overwrites.
-        if (need)
-          read_shared_slot<KEY>(n_after, base + (uint32_t)(u * kSlot), lane, pk);
-        else
-          wait_vm_n(n_after);
+        wait_vm_n(n_after);
         __builtin_amdgcn_s_barrier();
+        PageKeys<KEY> pk;
+        if (row_ok && j < live_w) read_shared_slot<KEY>(base + (uint32_t)(u * kSlot), lane, pk);
         issue(t + NS - 1);
         if (row_ok) {
           if (j >= live_w) {
