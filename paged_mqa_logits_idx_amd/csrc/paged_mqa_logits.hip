@@ -709,29 +709,35 @@ struct LdsPage {
   }
 };
 
-// One page of the shared table through LDS by DMA: wave w copies its quarter
-// of the key rows (16 B per lane, the XOR swizzle of LdsPage applied on the
-// source side since the DMA destination is lane-linear); wave 0 also copies
-// the 256 scale bytes (fp8).  Returns nothing; the wave's operation count per
-// page is kSharedDmaOps(w).
+// One page of the shared table through LDS by DMA: each of the kSharedRows
+// waves copies 64/kSharedRows of the key rows (16 B per lane, the XOR swizzle
+// of LdsPage applied on the source side since the DMA destination is
+// lane-linear); wave 0 also copies the 256 scale bytes (fp8).  The wave's
+// operation count per page is shared_dma_ops(wave).
+constexpr int kSharedRowsPerWave = kPage / kSharedRows;
+template <int KEY>
+constexpr int32_t shared_dma_ops(int wave) {
+  return (KEY == kBf16) ? kSharedRowsPerWave / 4 : kSharedRowsPerWave / 8 + (wave == 0 ? 1 : 0);
+}
 template <int KEY>
 __device__ __forceinline__ void shared_dma_page(const uint8_t* page, const uint8_t* scales, lds_u8* slot,
                                                 int wave, int lane) {
+  const int r0 = kSharedRowsPerWave * wave;
   if constexpr (KEY == kBf16) {
-    // 16 rows of 256 B per wave: 4 DMAs of 4 rows each
+    // rows of 256 B, 4 per DMA
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int i = 16 * wave + 4 * t + (lane >> 4), c = lane & 15;
+    for (int t = 0; t < kSharedRowsPerWave / 4; ++t) {
+      const int i = r0 + 4 * t + (lane >> 4), c = lane & 15;
       __builtin_amdgcn_global_load_lds((global_ptr)(page + i * 256 + 16 * (c ^ (i & 15))),
-                                       (lds_ptr)(slot + (16 * wave + 4 * t) * 256), 16, 0, 0);
+                                       (lds_ptr)(slot + (r0 + 4 * t) * 256), 16, 0, 0);
     }
   } else {
-    // 16 rows of 128 B per wave: 2 DMAs of 8 rows each
+    // rows of 128 B, 8 per DMA
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int i = 16 * wave + 8 * t + (lane >> 3), c = lane & 7;
+    for (int t = 0; t < kSharedRowsPerWave / 8; ++t) {
+      const int i = r0 + 8 * t + (lane >> 3), c = lane & 7;
       __builtin_amdgcn_global_load_lds((global_ptr)(page + i * 128 + 16 * (c ^ (i & 7))),
-                                       (lds_ptr)(slot + (16 * wave + 8 * t) * 128), 16, 0, 0);
+                                       (lds_ptr)(slot + (r0 + 8 * t) * 128), 16, 0, 0);
     }
     if (wave == 0)
       __builtin_amdgcn_global_load_lds((global_ptr)(scales + 4 * lane), (lds_ptr)(slot + 8192), 4, 0, 0);
@@ -827,7 +833,7 @@ __global__ __launch_bounds__(64 * kSharedRows) void shared_kernel(Params p, int3
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int32_t ops = (KEY == kFp8) ? (wave == 0 ? 3 : 2) : 4;  // DMA operations per page
+  const int32_t ops = shared_dma_ops<KEY>(wave);  // DMA operations per page
   const int32_t width = p.width;
   const int32_t* tab = p.pt;  // shared table (row stride 0)
 
@@ -883,7 +889,7 @@ __global__ __launch_bounds__(64 * kSharedRows) void shared_kernel(Params p, int3
       // still in flight, so that no conservative wait lands in the page loop.
       // (Wave 0 of the fp8 kernel has one more operation per page; waiting on
       // the smaller count there costs it a part of page 0, no more.)
-      __builtin_amdgcn_s_waitcnt(wait_vm((NS - 1) * ((KEY == kFp8) ? 2 : 4)));
+      __builtin_amdgcn_s_waitcnt(wait_vm((NS - 1) * shared_dma_ops<KEY>(1)));
       const int32_t st = row_ok ? 1 : 0;  // stores per iteration
       for (int32_t t = 0; j0 + t < jl; ++t) {
         const int32_t j = j0 + t;
