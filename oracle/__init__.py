@@ -49,6 +49,10 @@ class Oracle:
             ctypes.c_int, P, P, ctypes.c_int64, P, ctypes.c_int64, ctypes.c_int64, P,
             ctypes.c_int64, P, P, ctypes.c_int32, ctypes.c_int32, P, ctypes.c_int32, P]
         lib.oracle_paged_mqa_logits.restype = None
+        lib.oracle_e4m3fn_encode.argtypes = [ctypes.c_float]
+        lib.oracle_e4m3fn_encode.restype = ctypes.c_uint32
+        lib.oracle_quantize_keys_fp8.argtypes = [P, ctypes.c_int64, P, P]
+        lib.oracle_quantize_keys_fp8.restype = None
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
@@ -66,6 +70,19 @@ class Oracle:
 
     def set_num_threads(self, n: int) -> None:
         self.lib.oracle_set_num_threads(int(n))
+
+    def e4m3fn_encode(self, y: float) -> int:
+        return int(self.lib.oracle_e4m3fn_encode(float(y)))
+
+    def quantize_keys_fp8(self, keys_bits: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+        """e4m3fn codes [n, 128] and float32 scales [n] of bf16 keys (bits [n, 128])."""
+        k = np.ascontiguousarray(keys_bits, dtype=np.uint16).reshape(-1, 128)
+        n = k.shape[0]
+        codes = np.empty((n, 128), dtype=np.uint8)
+        scales = np.empty(n, dtype=np.float32)
+        if n:
+            self.lib.oracle_quantize_keys_fp8(k.ctypes.data, n, codes.ctypes.data, scales.ctypes.data)
+        return codes, scales
 
     def paged_mqa_logits(self, wl, rows=None) -> np.ndarray:
         """float64 logits [len(rows) or wl.rows, table_width*64] of a workload.
@@ -130,3 +147,11 @@ def set_num_threads(n: int) -> None:
 
 def paged_mqa_logits(wl, rows=None) -> np.ndarray:
     return default().paged_mqa_logits(wl, rows)
+
+
+def e4m3fn_encode(y: float) -> int:
+    return default().e4m3fn_encode(y)
+
+
+def quantize_keys_fp8(keys_bits: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    return default().quantize_keys_fp8(keys_bits)

@@ -148,6 +148,58 @@ void oracle_paged_mqa_logits(int key_kind, const uint16_t* q_bits, const uint8_t
 }
 
 /* Number of OpenMP threads the oracle runs with (1 when built without it). */
+/*
+ * Paged key store, fp8 (the write side of the cache block above): each key of
+ * 128 values gets one scale and 128 e4m3fn codes.  The pages give the block
+ * (64 positions x 128 fp8 values, then 64 fp32 scales) and a per-position
+ * scale; the quantiser itself is the reading taken for it -- scale = amax/448,
+ * the largest e4m3fn magnitude -- and every step is done in float32, in this
+ * order, so that a float32 implementation can match it bit for bit:
+ *
+ *   k_d    = the bf16 key value as float32 (exact)
+ *   amax   = max_d |k_d|
+ *   scale  = amax > 0 ? amax / 448 : 1                (float32 division)
+ *   y_d    = clamp(k_d / scale, -448, 448)            (float32 division)
+ *   code_d = e4m3fn nearest to y_d, ties to the even code; the sign of y_d is
+ *            kept when the nearest value is 0
+ */
+
+/* e4m3fn code nearest to y (|y| <= 448), ties to the code with mantissa LSB 0. */
+uint32_t oracle_e4m3fn_encode(float y) {
+  const double a = fabs((double)y);
+  uint32_t best = 0;
+  double best_d = INFINITY;
+  for (uint32_t c = 0; c <= 0x7Eu; ++c) {  /* the non-negative finite codes, ascending */
+    const double d = fabs(oracle_e4m3fn_value(c) - a);
+    if (d < best_d || (d == best_d && (c & 1u) == 0u)) {
+      best_d = d;
+      best = c;
+    }
+  }
+  return signbit(y) ? (best | 0x80u) : best;
+}
+
+void oracle_quantize_keys_fp8(const uint16_t* keys_bits, int64_t n, uint8_t* codes, float* scales) {
+  for (int64_t t = 0; t < n; ++t) {
+    float k[HD];
+    float amax = 0.0f;
+    for (int d = 0; d < HD; ++d) {
+      const uint32_t u = (uint32_t)keys_bits[t * HD + d] << 16;
+      memcpy(&k[d], &u, sizeof(float));
+      const float m = fabsf(k[d]);
+      if (m > amax) amax = m;
+    }
+    const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+    scales[t] = scale;
+    for (int d = 0; d < HD; ++d) {
+      float y = k[d] / scale;
+      if (y > 448.0f) y = 448.0f;
+      if (y < -448.0f) y = -448.0f;
+      codes[t * HD + d] = (uint8_t)oracle_e4m3fn_encode(y);
+    }
+  }
+}
+
 int oracle_num_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

@@ -404,6 +404,68 @@ def pin_pages_accuracy_bar(ora):
         assert smax == pages * P
 
 
+# --- key store (fp8 quantiser) ----------------------------------------------
+
+def _keys_bits(rng, n, scale=1.0):
+    k = (rng.standard_normal((n, D), dtype=np.float32) * np.float32(scale))
+    return torch.from_numpy(k).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _bits_to_f32(bits):
+    return (np.asarray(bits, dtype=np.uint32) << 16).view(np.float32)
+
+
+def pin_e4m3fn_encode_matches_library_cast(ora):
+    """Nearest-even encoding equals torch's float8_e4m3fn cast over a dense
+    sweep of [-448, 448] that includes every tie between neighbouring codes."""
+    vals = np.array([ora.e4m3fn_value(c) for c in range(0x7F)], dtype=np.float64)
+    mids = (vals[:-1] + vals[1:]) / 2  # ties: exactly representable in float32
+    ys = np.concatenate([mids, -mids, vals, -vals,
+                         np.linspace(-448, 448, 4001),
+                         np.arange(-64, 65) * 2.0 ** -12]).astype(np.float32)
+    ref = torch.from_numpy(ys).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([ora.e4m3fn_encode(float(y)) for y in ys], dtype=np.uint8)
+    assert np.array_equal(got, ref)
+
+
+def pin_e4m3fn_encode_round_trips_every_code(ora):
+    """Every finite code decodes to a value that encodes back to the same code."""
+    for c in list(range(0x7F)) + list(range(0x80, 0xFF)):
+        assert ora.e4m3fn_encode(ora.e4m3fn_value(c)) == c, hex(c)
+
+
+def pin_quantiser_matches_library_recipe(ora):
+    """Codes and scales equal the library route: scale = amax/448 in float32,
+    torch's e4m3fn cast of the clamped quotient (the generators' recipe)."""
+    rng = np.random.Generator(np.random.PCG64(7))
+    bits = np.concatenate([_keys_bits(rng, 200), _keys_bits(rng, 40, 1e-3), _keys_bits(rng, 40, 300.0)])
+    codes, scales = ora.quantize_keys_fp8(bits)
+    ref_codes, ref_scales = W.quantize_fp8(_bits_to_f32(bits))
+    assert np.array_equal(scales.view(np.uint32), ref_scales.view(np.uint32))
+    assert np.array_equal(codes, ref_codes)
+
+
+def pin_quantiser_closed_forms(ora):
+    """amax element -> +-448; one-hot key -> one code; zero key -> scale 1 and
+    codes 0; keys that are scale * (an e4m3fn value) come back exactly."""
+    one_hot = np.zeros((1, D), dtype=np.float32)
+    one_hot[0, 17] = -3.5
+    zero = np.zeros((1, D), dtype=np.float32)
+    rng = np.random.Generator(np.random.PCG64(8))
+    codes_in = rng.integers(0, 0x7F, size=(1, D))
+    codes_in[0, 5] = 0x7E  # 448 present: amax / 448 is exactly the scale
+    vals = np.array([ora.e4m3fn_value(int(c)) for c in codes_in[0]], dtype=np.float32)
+    exact = (vals * np.float32(0.25))[None, :]  # a power-of-two scale keeps bf16 exactness
+    k = np.concatenate([one_hot, zero, exact])
+    bits = torch.from_numpy(k).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(_bits_to_f32(bits), k)  # every input is exactly bf16
+    codes, scales = ora.quantize_keys_fp8(bits)
+    assert scales[0] == np.float32(3.5) / np.float32(448.0)
+    assert codes[0, 17] == 0xFE and np.all(np.delete(codes[0], 17) == 0)
+    assert scales[1] == 1.0 and np.all(codes[1] == 0)
+    assert scales[2] == np.float32(0.25) and np.array_equal(codes[2], codes_in[0].astype(np.uint8))
+
+
 # cheap pins first; the exact rational brute force last
 ALL_PINS = sorted((v for k, v in globals().items() if k.startswith("pin_")),
                   key=lambda f: (f is pin_exact_rational_brute_force, f.__name__))

@@ -40,6 +40,14 @@ MUTANTS = {
     "bad_page_not_nan": ("if (!page_ok) { o[i] = NAN; continue; }",
                          "if (!page_ok) { o[i] = 0.0; continue; }"),
     "bf16_keys_scaled": ("        s = 1.0;\n", "        s = 0.5;\n"),
+    "encode_ties_up": ("(d == best_d && (c & 1u) == 0u)", "(d == best_d)"),
+    "encode_zero_unsigned": ("return signbit(y) ? (best | 0x80u) : best;",
+                             "return y < 0.0f ? (best | 0x80u) : best;"),
+    "quant_scale_447": ("amax / 448.0f", "amax / 447.0f"),
+    "quant_amax_signed": ("const float m = fabsf(k[d]);", "const float m = k[d];"),
+    "quant_last_dim_dropped": ("for (int d = 0; d < HD; ++d) {\n      const uint32_t u",
+                               "for (int d = 0; d < HD - 1; ++d) {\n      const uint32_t u"),
+    "quant_zero_scale": ("amax > 0.0f ? amax / 448.0f : 1.0f", "amax / 448.0f"),
 }
 
 
