@@ -130,6 +130,45 @@ int idx_paged_mqa_logits_bf16(const void* q, const void* kv_pages, const float* 
                               int64_t kv_page_stride, int64_t kscale_page_stride,
                               int64_t page_table_row_stride, hipStream_t stream);
 
+/*
+ * Paged key store, fp8: the write side of the cache block above.  Each of n
+ * keys (128 values) is quantised and written to one slot of the pool.  The
+ * pages give the block (64 positions x 128 fp8 values, then 64 fp32 scales;
+ * "The Dispatch Wire ...", section "The Reasoning and Decision-Making") and a
+ * per-position scale; the quantiser is the amax/448 rule, computed in float32
+ * in this order (bit-exact, so every caller gets the same bytes):
+ *
+ *   scale   = amax > 0 ? amax / 448 : 1        amax = max_d |k_d|
+ *   code_d  = e4m3fn(clamp(k_d / scale, -448, 448)), round to nearest even;
+ *             a value that rounds to zero keeps its sign (0x80 for -0).
+ *
+ *   keys        bf16 [n][128], 16-byte aligned.
+ *   slots       int64 [n], 8-byte aligned: key t goes to page slots[t] / 64,
+ *               position slots[t] % 64.  A slot outside [0, 64*num_pages) --
+ *               e.g. -1 for a padding token -- skips the key.  Two keys with
+ *               the same slot race.
+ *   kv_pages    pool as in idx_paged_mqa_logits_fp8 (codes at page*stride +
+ *               128*position), 16-byte aligned; kv_page_stride >= 8192,
+ *               multiple of 16.
+ *   kscale      scales as in idx_paged_mqa_logits_fp8 (at page*kscale_page_stride
+ *               + 4*position), 4-byte aligned; kscale_page_stride >= 256,
+ *               multiple of 4.
+ *   n, num_pages  >= 0; n == 0 returns IDX_OK with no launch.
+ * Keys holding NaN or Inf give unspecified codes.
+ */
+int idx_store_keys_fp8(const void* keys, const int64_t* slots, int64_t n, void* kv_pages,
+                       float* kscale, int64_t num_pages, int64_t kv_page_stride,
+                       int64_t kscale_page_stride, hipStream_t stream);
+
+/*
+ * Paged key store, bf16: key t is copied to its slot of 16,384-byte bf16 pages
+ * (256 bytes per position, the bf16 store of "The Dispatch Decision ...",
+ * section "The Problem That Led Here").  Arguments as idx_store_keys_fp8
+ * without the scales; kv_page_stride >= 16384, multiple of 16.
+ */
+int idx_store_keys_bf16(const void* keys, const int64_t* slots, int64_t n, void* kv_pages,
+                        int64_t num_pages, int64_t kv_page_stride, hipStream_t stream);
+
 /* Static, human-readable text for an idx_status value (never NULL). */
 const char* idx_status_string(int status);
 

@@ -35,6 +35,8 @@ IDX_ERR_LAUNCH = -5
 _SYMBOLS = (
     "idx_paged_mqa_logits_fp8",
     "idx_paged_mqa_logits_bf16",
+    "idx_store_keys_fp8",
+    "idx_store_keys_bf16",
     "idx_status_string",
     "idx_abi_version",
 )
@@ -63,6 +65,14 @@ def _load() -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.argtypes = argtypes
         fn.restype = ctypes.c_int
+    lib.idx_store_keys_fp8.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
+    lib.idx_store_keys_fp8.restype = ctypes.c_int
+    lib.idx_store_keys_bf16.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+        ctypes.c_int64, ctypes.c_void_p]
+    lib.idx_store_keys_bf16.restype = ctypes.c_int
     lib.idx_status_string.argtypes = [ctypes.c_int]
     lib.idx_status_string.restype = ctypes.c_char_p
     lib.idx_abi_version.argtypes = []
@@ -167,7 +177,40 @@ def idx_paged_mqa_logits_bf16(q, kv_pages, kscale, page_table, seqlens, weights,
                  check=check)
 
 
+def idx_store_keys_fp8(keys, slots, kv_pages, kscale, *, num_pages, n=None,
+                       kv_page_stride=FP8_FUSED_PAGE_BYTES, kscale_page_stride=FP8_FUSED_PAGE_BYTES,
+                       stream=None, check=True) -> int:
+    """Quantise bf16 keys [n, 128] (scale = amax/448, e4m3fn codes) into pool slots.
+
+    ``slots`` is int64 [n] (64*page + position; out of range skips the key).
+    ``kscale`` is a tensor or a device address (fused block: kv_pages + 8192).
+    """
+    if n is None:
+        n = keys.shape[0]
+    dev = keys.device if isinstance(keys, torch.Tensor) else None
+    status = _lib.idx_store_keys_fp8(_addr(keys), _addr(slots), int(n), _addr(kv_pages),
+                                     _addr(kscale), int(num_pages), int(kv_page_stride),
+                                     int(kscale_page_stride), _stream_handle(stream, dev))
+    if check and status != IDX_OK:
+        raise IdxError(status, f"idx_store_keys_fp8: {idx_status_string(status)}")
+    return status
+
+
+def idx_store_keys_bf16(keys, slots, kv_pages, *, num_pages, n=None, kv_page_stride=BF16_PAGE_BYTES,
+                        stream=None, check=True) -> int:
+    """Copy bf16 keys [n, 128] into 16384-byte bf16 pages at the given slots."""
+    if n is None:
+        n = keys.shape[0]
+    dev = keys.device if isinstance(keys, torch.Tensor) else None
+    status = _lib.idx_store_keys_bf16(_addr(keys), _addr(slots), int(n), _addr(kv_pages),
+                                      int(num_pages), int(kv_page_stride), _stream_handle(stream, dev))
+    if check and status != IDX_OK:
+        raise IdxError(status, f"idx_store_keys_bf16: {idx_status_string(status)}")
+    return status
+
+
 __all__ = [
-    "idx_paged_mqa_logits_fp8", "idx_paged_mqa_logits_bf16", "idx_status_string",
+    "idx_paged_mqa_logits_fp8", "idx_paged_mqa_logits_bf16", "idx_store_keys_fp8",
+    "idx_store_keys_bf16", "idx_status_string",
     "idx_abi_version", "IdxError", "LIB_PATH", "NUM_HEADS", "HEAD_DIM", "PAGE_POSITIONS",
 ]

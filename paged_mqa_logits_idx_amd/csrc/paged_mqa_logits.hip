@@ -935,6 +935,74 @@ __global__ __launch_bounds__(64 * kSharedRows) void shared_kernel(Params p, int3
 }
 
 // ---------------------------------------------------------------------------
+// Paged key store: the write side of the cache block.  Key t (128 values)
+// goes to flat slot slots[t] = 64*page + i.  16 lanes per key, 8 values
+// (16 bytes of bf16) per lane, 4 keys per wave per step.  fp8: per key
+// scale = amax/448 (1 for an all-zero key) and the e4m3fn codes of the
+// quotient clamped to +-448, every step in float32; bf16: a copy.
+constexpr int kStoreWaves = 4;
+
+template <int KEY>
+__global__ __launch_bounds__(64 * kStoreWaves) void store_keys_kernel(const uint8_t* keys, const int64_t* slots,
+                                                                     int64_t n, uint8_t* kv, uint8_t* ks,
+                                                                     int64_t num_pages, int64_t kv_stride,
+                                                                     int64_t ks_stride) {
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 15;  // 16-byte part of the key
+  const int64_t groups = ((int64_t)gridDim.x * kStoreWaves) * 4;
+  for (int64_t t0 = ((int64_t)blockIdx.x * kStoreWaves + (threadIdx.x >> 6)) * 4; t0 < n; t0 += groups) {
+    const int64_t t = t0 + (lane >> 4);
+    int64_t slot = -1;
+    u32x4 raw = {0u, 0u, 0u, 0u};
+    if (t < n) {
+      slot = slots[t];
+      raw = *reinterpret_cast<const u32x4*>(keys + t * (kDim * 2) + 16 * c);
+    }
+    const bool ok = t < n && slot >= 0 && slot < num_pages * kPage;
+    const int64_t g = ok ? slot / kPage : 0;
+    const int i = ok ? (int)(slot % kPage) : 0;
+    if constexpr (KEY == kBf16) {
+      if (ok) *reinterpret_cast<u32x4*>(kv + g * kv_stride + (int64_t)i * (kDim * 2) + 16 * c) = raw;
+    } else {
+      float v[8];
+      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v[2 * k] = __builtin_bit_cast(float, w[k] << 16);
+        v[2 * k + 1] = __builtin_bit_cast(float, w[k] & 0xffff0000u);
+      }
+      float m = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(v[k]));
+      // amax over the key's 16 lanes (the xor masks stay inside a 16-lane group)
+      m = fmaxf(m, __shfl_xor(m, 8));
+      m = fmaxf(m, __shfl_xor(m, 4));
+      m = fmaxf(m, __shfl_xor(m, 2));
+      m = fmaxf(m, __shfl_xor(m, 1));
+      const float scale = m > 0.0f ? m / 448.0f : 1.0f;
+      uint32_t out[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        float y[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) y[k] = fminf(fmaxf(v[4 * h + k] / scale, -448.0f), 448.0f);
+        uint32_t code = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+        code = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], (int)code, true);
+        // a value that rounds to zero keeps its sign (0x80 for -0)
+        uint32_t sign = 0u;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) sign |= (__builtin_bit_cast(uint32_t, y[k]) >> 31) << (8 * k + 7);
+        out[h] = code | sign;
+      }
+      if (ok) {
+        *reinterpret_cast<uint2*>(kv + g * kv_stride + (int64_t)i * kDim + 8 * c) = make_uint2(out[0], out[1]);
+        if (c == 0) *reinterpret_cast<float*>(ks + g * ks_stride + 4 * i) = scale;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host side.
 
 constexpr int kRowwisePPW = 2;
@@ -1049,6 +1117,32 @@ int launch(const void* q, const void* kv_pages, const float* kscale, const int32
   return hipGetLastError() == hipSuccess ? IDX_OK : IDX_ERR_LAUNCH;
 }
 
+template <int KEY>
+int store_keys(const void* keys, const int64_t* slots, int64_t n, void* kv_pages, float* kscale,
+               int64_t num_pages, int64_t kv_page_stride, int64_t kscale_page_stride,
+               hipStream_t stream) {
+  if (n < 0 || num_pages < 0) return IDX_ERR_SHAPE;
+  const int64_t min_kv = (KEY == kFp8) ? (int64_t)kPage * kDim : (int64_t)kPage * kDim * 2;
+  if (kv_page_stride < min_kv || kv_page_stride > ((int64_t)1 << 32)) return IDX_ERR_SHAPE;
+  if (KEY == kFp8 && (kscale_page_stride < kPage * 4 || kscale_page_stride > ((int64_t)1 << 32)))
+    return IDX_ERR_SHAPE;
+  if (n == 0) return IDX_OK;
+  if (!keys || !slots || !kv_pages) return IDX_ERR_NULL;
+  if (KEY == kFp8 ? (kscale == nullptr) : (kscale != nullptr)) return IDX_ERR_NULL;
+  if (!aligned(keys, 16) || !aligned(slots, 8) || !aligned(kv_pages, 16) || (kv_page_stride % 16) != 0)
+    return IDX_ERR_ALIGN;
+  if (KEY == kFp8 && (!aligned(kscale, 4) || (kscale_page_stride % 4) != 0)) return IDX_ERR_ALIGN;
+  (void)hipGetLastError();
+  const int64_t want = (n + 4 * kStoreWaves - 1) / (4 * kStoreWaves);
+  const int64_t cap = (int64_t)8 * device_cu_count();
+  const int64_t grid = want < cap ? want : cap;
+  store_keys_kernel<KEY><<<dim3((uint32_t)grid), dim3(64 * kStoreWaves), 0, stream>>>(
+      static_cast<const uint8_t*>(keys), slots, n, static_cast<uint8_t*>(kv_pages),
+      reinterpret_cast<uint8_t*>(kscale), num_pages, kv_page_stride,
+      (KEY == kFp8) ? kscale_page_stride : 0);
+  return hipGetLastError() == hipSuccess ? IDX_OK : IDX_ERR_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1073,6 +1167,18 @@ int idx_paged_mqa_logits_bf16(const void* q, const void* kv_pages, const float* 
   return launch<kBf16>(q, kv_pages, kscale, page_table, seqlens, weights, out, rows, num_heads,
                        head_dim, table_width, num_pages, kv_page_stride, kscale_page_stride,
                        page_table_row_stride, stream);
+}
+
+int idx_store_keys_fp8(const void* keys, const int64_t* slots, int64_t n, void* kv_pages, float* kscale,
+                       int64_t num_pages, int64_t kv_page_stride, int64_t kscale_page_stride,
+                       hipStream_t stream) {
+  return store_keys<kFp8>(keys, slots, n, kv_pages, kscale, num_pages, kv_page_stride,
+                          kscale_page_stride, stream);
+}
+
+int idx_store_keys_bf16(const void* keys, const int64_t* slots, int64_t n, void* kv_pages,
+                        int64_t num_pages, int64_t kv_page_stride, hipStream_t stream) {
+  return store_keys<kBf16>(keys, slots, n, kv_pages, nullptr, num_pages, kv_page_stride, 0, stream);
 }
 
 const char* idx_status_string(int status) {

@@ -144,3 +144,25 @@ def assert_parity(got, ref, mask=None, atol=ATOL, rtol=RTOL, label=""):
     assert st["max_abs"] <= atol, msg
     assert st["rel"] <= rtol, msg
     return st
+
+
+def random_slot_workload(rng, rows: int, width: int, num_pages: int):
+    """fp8 workload whose pool is left empty for the key store to fill.
+
+    Returns (workload, keys as bf16 bits [n, 128], slots [n]) with one key for
+    every slot of the pool in a random order; q, w, tables and lengths are
+    random (tables draw distinct pages per row).
+    """
+    q = W.to_bf16_bits(rng.standard_normal((rows, W.NUM_HEADS, W.HEAD_DIM), dtype=np.float32))
+    w = (rng.standard_normal((rows, W.NUM_HEADS)) / 8).astype(np.float32)
+    table = np.stack([rng.permutation(num_pages)[:width] for _ in range(rows)]).astype(np.int32)
+    seqlens = rng.integers(1, width * W.PAGE + 1, size=rows).astype(np.int32)
+    n = num_pages * W.PAGE
+    bits = W.to_bf16_bits(rng.standard_normal((n, W.HEAD_DIM), dtype=np.float32))
+    slots = rng.permutation(n).astype(np.int64)
+    kv = np.zeros(num_pages * W.FP8_FUSED_STRIDE, dtype=np.uint8)
+    wl = W.Workload(name="stored keys", key_kind="fp8", rows=rows, table_width=width,
+                    num_pages=num_pages, q=q, weights=w, kv=kv, kv_stride=W.FP8_FUSED_STRIDE,
+                    ks=kv, ks_offset=W.FP8_KEY_BYTES, ks_stride=W.FP8_FUSED_STRIDE,
+                    page_table=table.reshape(-1).copy(), pt_stride=width, seqlens=seqlens)
+    return wl, bits, slots

@@ -32,6 +32,13 @@ def lib():
     for name in ("idx_paged_mqa_logits_fp8", "idx_paged_mqa_logits_bf16"):
         getattr(l, name).argtypes = args
         getattr(l, name).restype = ctypes.c_int
+    l.idx_store_keys_fp8.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                     ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                     ctypes.c_void_p]
+    l.idx_store_keys_fp8.restype = ctypes.c_int
+    l.idx_store_keys_bf16.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                      ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
+    l.idx_store_keys_bf16.restype = ctypes.c_int
     l.idx_status_string.restype = ctypes.c_char_p
     l.idx_status_string.argtypes = [ctypes.c_int]
     return l
@@ -40,7 +47,7 @@ def lib():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "idx_abi_version", "idx_paged_mqa_logits_bf16", "idx_paged_mqa_logits_fp8",
-        "idx_status_string"])
+        "idx_status_string", "idx_store_keys_bf16", "idx_store_keys_fp8"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -107,3 +114,41 @@ FP8, BF16 = "idx_paged_mqa_logits_fp8", "idx_paged_mqa_logits_bf16"
 ])
 def test_host_validation(lib, name, kw, status):
     assert _call(lib, name, **kw) == status
+
+
+def _store(lib, name, **kw):
+    a = dict(keys=16, slots=8, n=1, kv=16, ks=16, num_pages=1, kv_stride=8448, ks_stride=8448)
+    if name.endswith("bf16"):
+        a.update(kv_stride=16384)
+    a.update(kw)
+    if name.endswith("bf16"):
+        return lib.idx_store_keys_bf16(a["keys"], a["slots"], a["n"], a["kv"], a["num_pages"],
+                                       a["kv_stride"], None)
+    return lib.idx_store_keys_fp8(a["keys"], a["slots"], a["n"], a["kv"], a["ks"], a["num_pages"],
+                                  a["kv_stride"], a["ks_stride"], None)
+
+
+SF, SB = "idx_store_keys_fp8", "idx_store_keys_bf16"
+
+
+@pytest.mark.parametrize("name,kw,status", [
+    (SF, dict(n=-1), IDX_ERR_SHAPE),
+    (SF, dict(num_pages=-1), IDX_ERR_SHAPE),
+    (SF, dict(kv_stride=8191), IDX_ERR_SHAPE),
+    (SF, dict(ks_stride=255), IDX_ERR_SHAPE),
+    (SB, dict(kv_stride=8448), IDX_ERR_SHAPE),
+    (SF, dict(n=0, keys=None, slots=None, kv=None, ks=None), IDX_OK),   # nothing to store
+    (SF, dict(keys=None), IDX_ERR_NULL),
+    (SF, dict(slots=None), IDX_ERR_NULL),
+    (SF, dict(kv=None), IDX_ERR_NULL),
+    (SF, dict(ks=None), IDX_ERR_NULL),
+    (SB, dict(kv=None), IDX_ERR_NULL),
+    (SF, dict(keys=8), IDX_ERR_ALIGN),
+    (SF, dict(slots=4), IDX_ERR_ALIGN),
+    (SF, dict(kv=20), IDX_ERR_ALIGN),
+    (SF, dict(ks=18), IDX_ERR_ALIGN),
+    (SF, dict(kv_stride=8456), IDX_ERR_ALIGN),
+    (SF, dict(ks_stride=8450), IDX_ERR_ALIGN),
+])
+def test_store_host_validation(lib, name, kw, status):
+    assert _store(lib, name, **kw) == status
