@@ -142,6 +142,60 @@ def measure(cfg, steps: int, warmup: int):
     return wl, res
 
 
+def measure_store(steps: int, warmup: int):
+    """fp8 key store: every slot of the 32,768-page pool (2,097,152 keys) per step.
+
+    Keys arrive the way a prefill writes them: page after page of a request,
+    pages in a random pool order, the 64 positions of a page in order.
+    """
+    import torch
+
+    import paged_mqa_logits_idx_amd as lib
+    import workloads as W
+
+    num_pages = 32768
+    n = num_pages * W.PAGE
+    g = torch.Generator(device="cuda").manual_seed(1234)
+    keys = torch.randn((n, W.HEAD_DIM), device="cuda", generator=g).to(torch.bfloat16)
+    page_order = torch.randperm(num_pages, device="cuda", generator=g).to(torch.int64)
+    slots = (page_order[:, None] * W.PAGE + torch.arange(W.PAGE, device="cuda")[None, :]).reshape(-1)
+    pools = [torch.empty(num_pages * W.FP8_FUSED_STRIDE, dtype=torch.uint8, device="cuda")
+             for _ in range(4)]  # rotate: 4 x 277 MB of destinations
+
+    def step(i):
+        pool = pools[i % len(pools)]
+        lib.idx_store_keys_fp8(keys, slots, pool, pool.data_ptr() + W.FP8_KEY_BYTES,
+                               num_pages=num_pages)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(warmup):
+            step(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(steps):
+            step(i)
+    graph.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    graph.replay()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    per_key = W.HEAD_DIM * 2 + 8 + W.HEAD_DIM + 4  # bf16 key + slot id in, codes + scale out
+    alg = n * per_key
+    del graph, pools, keys, slots
+    torch.cuda.empty_cache()
+    return {"workload": f"fp8 key store, {n} keys into a {num_pages}-page pool (whole pages)",
+            "kernel_ms_mean": round(ms, 5), "keys_per_s": n / (ms * 1e-3), "bound": "hbm",
+            "achieved_gbs": round(alg / (ms * 1e-3) / 1e9, 1), "peak_gbs": HBM_PEAK_GBS,
+            "frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "alg_bytes": alg}
+
+
 def cpu_baseline(wl, target_s: float):
     """The oracle, as it stands, on a bounded sample of rows of the same workload."""
     import numpy as np
@@ -244,6 +298,9 @@ def main() -> int:
                              frac=round(r["gbs"] / HBM_PEAK_GBS, 4),
                              alg_bytes=r["alg_read_bytes"] + r["alg_write_bytes"])
             secondary[str(c)] = entry
+        r = measure_store(max(10, args.steps // 2), max(3, args.warmup // 2))
+        log(json.dumps(r))
+        secondary["store_fp8"] = r
 
     cpu = None
     if not args.no_cpu_baseline:

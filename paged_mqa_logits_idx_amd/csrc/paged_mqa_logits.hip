@@ -941,6 +941,7 @@ __global__ __launch_bounds__(64 * kSharedRows) void shared_kernel(Params p, int3
 // scale = amax/448 (1 for an all-zero key) and the e4m3fn codes of the
 // quotient clamped to +-448, every step in float32; bf16: a copy.
 constexpr int kStoreWaves = 4;
+constexpr int kStoreUnroll = 4;  // groups of 4 keys per wave and iteration
 
 template <int KEY>
 __global__ __launch_bounds__(64 * kStoreWaves) void store_keys_kernel(const uint8_t* keys, const int64_t* slots,
@@ -949,54 +950,65 @@ __global__ __launch_bounds__(64 * kStoreWaves) void store_keys_kernel(const uint
                                                                      int64_t ks_stride) {
   const int lane = threadIdx.x & 63;
   const int c = lane & 15;  // 16-byte part of the key
-  const int64_t groups = ((int64_t)gridDim.x * kStoreWaves) * 4;
-  for (int64_t t0 = ((int64_t)blockIdx.x * kStoreWaves + (threadIdx.x >> 6)) * 4; t0 < n; t0 += groups) {
-    const int64_t t = t0 + (lane >> 4);
-    int64_t slot = -1;
-    u32x4 raw = {0u, 0u, 0u, 0u};
-    if (t < n) {
-      slot = slots[t];
-      raw = *reinterpret_cast<const u32x4*>(keys + t * (kDim * 2) + 16 * c);
+  const int64_t wave_id = (int64_t)blockIdx.x * kStoreWaves + (threadIdx.x >> 6);
+  const int64_t step = (int64_t)gridDim.x * kStoreWaves * 4 * kStoreUnroll;
+  // kStoreUnroll groups of 4 keys per iteration: all their loads are issued
+  // before the first group is quantised, so a wave has that many in flight.
+  for (int64_t base = wave_id * 4 * kStoreUnroll; base < n; base += step) {
+    int64_t slot[kStoreUnroll];
+    u32x4 raw[kStoreUnroll];
+#pragma unroll
+    for (int u = 0; u < kStoreUnroll; ++u) {
+      const int64_t t = base + 4 * u + (lane >> 4);
+      slot[u] = -1;
+      raw[u] = (u32x4){0u, 0u, 0u, 0u};
+      if (t < n) {
+        slot[u] = slots[t];
+        raw[u] = *reinterpret_cast<const u32x4*>(keys + t * (kDim * 2) + 16 * c);
+      }
     }
-    const bool ok = t < n && slot >= 0 && slot < num_pages * kPage;
-    const int64_t g = ok ? slot / kPage : 0;
-    const int i = ok ? (int)(slot % kPage) : 0;
-    if constexpr (KEY == kBf16) {
-      if (ok) *reinterpret_cast<u32x4*>(kv + g * kv_stride + (int64_t)i * (kDim * 2) + 16 * c) = raw;
-    } else {
-      float v[8];
-      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        v[2 * k] = __builtin_bit_cast(float, w[k] << 16);
-        v[2 * k + 1] = __builtin_bit_cast(float, w[k] & 0xffff0000u);
-      }
-      float m = 0.0f;
+    for (int u = 0; u < kStoreUnroll; ++u) {
+      const bool ok = slot[u] >= 0 && slot[u] < num_pages * kPage;  // (slot -1 past n)
+      const int64_t g = ok ? slot[u] / kPage : 0;
+      const int i = ok ? (int)(slot[u] % kPage) : 0;
+      if constexpr (KEY == kBf16) {
+        if (ok) *reinterpret_cast<u32x4*>(kv + g * kv_stride + (int64_t)i * (kDim * 2) + 16 * c) = raw[u];
+      } else {
+        float v[8];
+        const uint32_t w[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
 #pragma unroll
-      for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(v[k]));
-      // amax over the key's 16 lanes (the xor masks stay inside a 16-lane group)
-      m = fmaxf(m, __shfl_xor(m, 8));
-      m = fmaxf(m, __shfl_xor(m, 4));
-      m = fmaxf(m, __shfl_xor(m, 2));
-      m = fmaxf(m, __shfl_xor(m, 1));
-      const float scale = m > 0.0f ? m / 448.0f : 1.0f;
-      uint32_t out[2];
+        for (int k = 0; k < 4; ++k) {
+          v[2 * k] = __builtin_bit_cast(float, w[k] << 16);
+          v[2 * k + 1] = __builtin_bit_cast(float, w[k] & 0xffff0000u);
+        }
+        float m = 0.0f;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        float y[4];
+        for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(v[k]));
+        // amax over the key's 16 lanes (the xor masks stay inside a 16-lane group)
+        m = fmaxf(m, __shfl_xor(m, 8));
+        m = fmaxf(m, __shfl_xor(m, 4));
+        m = fmaxf(m, __shfl_xor(m, 2));
+        m = fmaxf(m, __shfl_xor(m, 1));
+        const float scale = m > 0.0f ? m / 448.0f : 1.0f;
+        uint32_t out[2];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) y[k] = fminf(fmaxf(v[4 * h + k] / scale, -448.0f), 448.0f);
-        uint32_t code = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
-        code = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], (int)code, true);
-        // a value that rounds to zero keeps its sign (0x80 for -0)
-        uint32_t sign = 0u;
+        for (int h = 0; h < 2; ++h) {
+          float y[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) sign |= (__builtin_bit_cast(uint32_t, y[k]) >> 31) << (8 * k + 7);
-        out[h] = code | sign;
-      }
-      if (ok) {
-        *reinterpret_cast<uint2*>(kv + g * kv_stride + (int64_t)i * kDim + 8 * c) = make_uint2(out[0], out[1]);
-        if (c == 0) *reinterpret_cast<float*>(ks + g * ks_stride + 4 * i) = scale;
+          for (int k = 0; k < 4; ++k) y[k] = fminf(fmaxf(v[4 * h + k] / scale, -448.0f), 448.0f);
+          uint32_t code = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+          code = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], (int)code, true);
+          // a value that rounds to zero keeps its sign (0x80 for -0)
+          uint32_t sign = 0u;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) sign |= (__builtin_bit_cast(uint32_t, y[k]) >> 31) << (8 * k + 7);
+          out[h] = code | sign;
+        }
+        if (ok) {
+          *reinterpret_cast<uint2*>(kv + g * kv_stride + (int64_t)i * kDim + 8 * c) = make_uint2(out[0], out[1]);
+          if (c == 0) *reinterpret_cast<float*>(ks + g * ks_stride + 4 * i) = scale;
+        }
       }
     }
   }
@@ -1133,7 +1145,7 @@ int store_keys(const void* keys, const int64_t* slots, int64_t n, void* kv_pages
     return IDX_ERR_ALIGN;
   if (KEY == kFp8 && (!aligned(kscale, 4) || (kscale_page_stride % 4) != 0)) return IDX_ERR_ALIGN;
   (void)hipGetLastError();
-  const int64_t want = (n + 4 * kStoreWaves - 1) / (4 * kStoreWaves);
+  const int64_t want = (n + 4 * kStoreWaves * kStoreUnroll - 1) / (4 * kStoreWaves * kStoreUnroll);
   const int64_t cap = (int64_t)8 * device_cu_count();
   const int64_t grid = want < cap ? want : cap;
   store_keys_kernel<KEY><<<dim3((uint32_t)grid), dim3(64 * kStoreWaves), 0, stream>>>(
