@@ -53,6 +53,9 @@ class Oracle:
         lib.oracle_e4m3fn_encode.restype = ctypes.c_uint32
         lib.oracle_quantize_keys_fp8.argtypes = [P, ctypes.c_int64, P, P]
         lib.oracle_quantize_keys_fp8.restype = None
+        lib.oracle_topk.argtypes = [P, ctypes.c_int64, P, ctypes.c_int32, ctypes.c_int32,
+                                    ctypes.c_int32, P]
+        lib.oracle_topk.restype = None
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
@@ -83,6 +86,24 @@ class Oracle:
         if n:
             self.lib.oracle_quantize_keys_fp8(k.ctypes.data, n, codes.ctypes.data, scales.ctypes.data)
         return codes, scales
+
+    def topk(self, values: np.ndarray, seqlens, k: int) -> np.ndarray:
+        """int32 [rows, k]: per row, the k largest of values[b, :L] (ties and NaN
+        as oracle.c states), in ascending position order, then -1 padding."""
+        v = np.ascontiguousarray(values, dtype=np.float64)
+        if v.ndim != 2:
+            raise ValueError("values must be [rows, ncols]")
+        rows, ncols = v.shape
+        sl = np.ascontiguousarray(np.asarray(seqlens, dtype=np.int32).reshape(-1))
+        if sl.size != rows:
+            raise ValueError("one seqlen per row")
+        if k < 0:
+            raise ValueError("k must be >= 0")
+        idx = np.empty((rows, k), dtype=np.int32)
+        if rows and k:
+            self.lib.oracle_topk(v.ctypes.data, ncols, sl.ctypes.data, rows, ncols, int(k),
+                                 idx.ctypes.data)
+        return idx
 
     def paged_mqa_logits(self, wl, rows=None) -> np.ndarray:
         """float64 logits [len(rows) or wl.rows, table_width*64] of a workload.
@@ -155,3 +176,7 @@ def e4m3fn_encode(y: float) -> int:
 
 def quantize_keys_fp8(keys_bits: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     return default().quantize_keys_fp8(keys_bits)
+
+
+def topk(values: np.ndarray, seqlens, k: int) -> np.ndarray:
+    return default().topk(values, seqlens, k)

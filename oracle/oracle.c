@@ -37,6 +37,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
@@ -147,7 +148,6 @@ void oracle_paged_mqa_logits(int key_kind, const uint16_t* q_bits, const uint8_t
   }
 }
 
-/* Number of OpenMP threads the oracle runs with (1 when built without it). */
 /*
  * Paged key store, fp8 (the write side of the cache block above): each key of
  * 128 values gets one scale and 128 e4m3fn codes.  The pages give the block
@@ -200,6 +200,66 @@ void oracle_quantize_keys_fp8(const uint16_t* keys_bits, int64_t n, uint8_t* cod
   }
 }
 
+/*
+ * Top-k selection over logits rows, the consumer of the -inf-masked output
+ * ("The Final Gate: Validating a Custom Triton Indexer Kernel Before
+ * Production Deployment", section "What the Test Output Reveals": the masking
+ * matters because the logits feed a downstream top-k).  The pages give no k
+ * and no tie rule; the readings taken:
+ *
+ *   candidates   positions p < L, L = clamp(seqlen, 0, ncols)
+ *   order        larger value first; equal values (-0 equals +0) by lower
+ *                position; NaN after every number
+ *   output       the first min(k, L) candidates of that order, written in
+ *                ascending position order, then -1 up to k
+ *
+ * The values are given as float64 (float32 logits convert exactly, with the
+ * same order).
+ */
+struct topk_cand {
+  double v;
+  int32_t p;
+};
+
+static int topk_rank_cmp(const void* a, const void* b) {
+  const struct topk_cand* x = (const struct topk_cand*)a;
+  const struct topk_cand* y = (const struct topk_cand*)b;
+  const int xn = isnan(x->v) ? 1 : 0, yn = isnan(y->v) ? 1 : 0;
+  if (xn != yn) return xn - yn;
+  if (!xn && x->v != y->v) return x->v > y->v ? -1 : 1;
+  return (x->p > y->p) - (x->p < y->p);
+}
+
+static int topk_pos_cmp(const void* a, const void* b) {
+  const int32_t x = *(const int32_t*)a, y = *(const int32_t*)b;
+  return (x > y) - (x < y);
+}
+
+void oracle_topk(const double* vals, int64_t row_stride, const int32_t* seqlens, int32_t rows,
+                 int32_t ncols, int32_t k, int32_t* idx) {
+#pragma omp parallel for schedule(dynamic)
+  for (int32_t b = 0; b < rows; ++b) {
+    int32_t L = seqlens[b];
+    if (L < 0) L = 0;
+    if (L > ncols) L = ncols;
+    const int32_t m = L < k ? L : k;
+    int32_t* o = idx + (int64_t)b * k;
+    if (m > 0) {
+      struct topk_cand* c = (struct topk_cand*)malloc(sizeof(struct topk_cand) * (size_t)L);
+      for (int32_t p = 0; p < L; ++p) {
+        c[p].v = vals[(int64_t)b * row_stride + p];
+        c[p].p = p;
+      }
+      qsort(c, (size_t)L, sizeof(struct topk_cand), topk_rank_cmp);
+      for (int32_t t = 0; t < m; ++t) o[t] = c[t].p;
+      free(c);
+      qsort(o, (size_t)m, sizeof(int32_t), topk_pos_cmp);
+    }
+    for (int32_t t = m; t < k; ++t) o[t] = -1;
+  }
+}
+
+/* Number of OpenMP threads the oracle runs with (1 when built without it). */
 int oracle_num_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

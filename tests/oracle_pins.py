@@ -466,6 +466,105 @@ def pin_quantiser_closed_forms(ora):
     assert scales[2] == np.float32(0.25) and np.array_equal(codes[2], codes_in[0].astype(np.uint8))
 
 
+# ---------------------------------------------------------------------------
+# top-k over the logits
+
+def _brute_topk(vals, L, k):
+    """Exhaustive search over every index set of size min(k, L) in [0, L):
+    keep the sets whose values, listed largest first (NaN below every number),
+    form the largest sequence, and of those the set whose sorted positions form
+    the smallest sequence."""
+    import itertools
+
+    def desc(ix):
+        return sorted(((0, 0.0) if math.isnan(vals[i]) else (1, float(vals[i])) for i in ix),
+                      reverse=True)
+
+    m = min(k, max(L, 0))
+    best = None
+    for ix in itertools.combinations(range(max(L, 0)), m):
+        key = desc(ix)
+        if best is None or key > best[0] or (key == best[0] and list(ix) < best[1]):
+            best = (key, list(ix))
+    return best[1] + [-1] * (k - m)
+
+
+def pin_topk_brute_force_tiny(ora):
+    """Rows of at most 8 values drawn from a small set (repeats, +-0, NaN,
+    +-inf), any length and k: the oracle equals exhaustive search."""
+    rng = np.random.Generator(np.random.PCG64(21))
+    pool = np.array([0.0, -0.0, 1.0, -1.0, 2.5, np.nan, np.inf, -np.inf], dtype=np.float32)
+    for _ in range(400):
+        ncols = int(rng.integers(1, 9))
+        k = int(rng.integers(0, 7))
+        vals = pool[rng.integers(0, len(pool), size=(1, ncols))]
+        L = int(rng.integers(-2, ncols + 3))
+        got = ora.topk(vals, [L], k)[0].tolist()
+        want = _brute_topk(vals[0], min(L, ncols), k)
+        assert got == want, (vals.tolist(), L, k, got, want)
+
+
+def pin_topk_matches_library_topk(ora):
+    """Distinct values: the set equals torch.topk's (a library routine), in
+    ascending position order; rows shorter than k return every position."""
+    rng = np.random.Generator(np.random.PCG64(22))
+    rows, ncols, k = 6, 5000, 2048
+    vals = rng.permutation(rows * ncols).reshape(rows, ncols).astype(np.float32) - 7000.0
+    seqlens = np.array([5000, 4000, 2049, 2048, 100, 0], dtype=np.int32)
+    got = ora.topk(vals, seqlens, k)
+    for b in range(rows):
+        L = int(seqlens[b])
+        if L >= k:
+            ref = torch.topk(torch.from_numpy(vals[b, :L]), k).indices.sort().values.numpy()
+            assert np.array_equal(got[b], ref)
+        else:
+            assert np.array_equal(got[b, :L], np.arange(L)) and np.all(got[b, L:] == -1)
+
+
+def pin_topk_closed_forms(ora):
+    """Equal values -> the first k positions; increasing -> the last k of
+    [0, L); decreasing -> the first k; L <= 0 -> all -1; seqlen past the row
+    clamps to it; +0 and -0 tie; NaN ranks below -inf."""
+    n, k = 50, 7
+    eq = np.full((1, n), 3.0, dtype=np.float32)
+    inc = np.arange(n, dtype=np.float32)[None, :]
+    assert ora.topk(eq, [n], k)[0].tolist() == list(range(k))
+    assert ora.topk(inc, [30], k)[0].tolist() == list(range(23, 30))
+    assert ora.topk(-inc, [30], k)[0].tolist() == list(range(k))
+    assert ora.topk(inc, [0], k)[0].tolist() == [-1] * k
+    assert ora.topk(inc, [-5], k)[0].tolist() == [-1] * k
+    assert ora.topk(inc, [10 ** 6], 3)[0].tolist() == [n - 3, n - 2, n - 1]
+    zeros = np.array([[-0.0, 0.0, -0.0, 0.0]], dtype=np.float32)
+    assert ora.topk(zeros, [4], 2)[0].tolist() == [0, 1]
+    nan = np.array([[np.nan, 1.0, np.nan, -np.inf]], dtype=np.float32)
+    assert ora.topk(nan, [4], 2)[0].tolist() == [1, 3]
+    assert ora.topk(nan, [4], 3)[0].tolist() == [0, 1, 3]
+    assert ora.topk(nan, [4], 0).shape == (1, 0)
+
+
+def pin_topk_threshold_split(ora):
+    """Large rows with many ties: every selected value is >= every candidate
+    left out, and of the values equal to the k-th largest the selected ones
+    are those at the lowest positions."""
+    rng = np.random.Generator(np.random.PCG64(23))
+    rows, ncols, k = 4, 20000, 2048
+    vals = np.round(rng.standard_normal((rows, ncols)) * 3, 1).astype(np.float32)
+    seqlens = np.array([20000, 15000, 3000, 2100], dtype=np.int32)
+    got = ora.topk(vals, seqlens, k)
+    for b in range(rows):
+        L = int(seqlens[b])
+        sel = got[b]
+        assert np.all(np.diff(sel) > 0) and sel[0] >= 0 and sel[-1] < L
+        mask = np.zeros(L, dtype=bool)
+        mask[sel] = True
+        v = vals[b, :L]
+        kth = np.sort(v)[::-1][k - 1]
+        assert v[mask].min() == kth and v[~mask].max() <= kth
+        tied = np.flatnonzero(v == kth)
+        n_above = int((v > kth).sum())
+        assert np.array_equal(np.flatnonzero(mask & (v == kth)), tied[:k - n_above])
+
+
 # cheap pins first; the exact rational brute force last
 ALL_PINS = sorted((v for k, v in globals().items() if k.startswith("pin_")),
                   key=lambda f: (f is pin_exact_rational_brute_force, f.__name__))

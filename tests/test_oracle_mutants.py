@@ -48,6 +48,19 @@ MUTANTS = {
     "quant_last_dim_dropped": ("for (int d = 0; d < HD; ++d) {\n      const uint32_t u",
                                "for (int d = 0; d < HD - 1; ++d) {\n      const uint32_t u"),
     "quant_zero_scale": ("amax > 0.0f ? amax / 448.0f : 1.0f", "amax / 448.0f"),
+    "topk_ties_to_high_position": ("return (x->p > y->p) - (x->p < y->p);",
+                                   "return (x->p < y->p) - (x->p > y->p);"),
+    "topk_nan_first": ("if (xn != yn) return xn - yn;", "if (xn != yn) return yn - xn;"),
+    "topk_smallest": ("return x->v > y->v ? -1 : 1;", "return x->v < y->v ? -1 : 1;"),
+    "topk_ignores_length": ("    int32_t L = seqlens[b];\n    if (L < 0) L = 0;\n    if (L > ncols) L = ncols;\n    const int32_t m",
+                            "    int32_t L = ncols;\n    const int32_t m"),
+    "topk_rank_order_output": ("      qsort(o, (size_t)m, sizeof(int32_t), topk_pos_cmp);\n", ""),
+    "topk_signed_zero_ordered": (
+        "  if (!xn && x->v != y->v) return x->v > y->v ? -1 : 1;\n",
+        "  if (!xn && x->v != y->v) return x->v > y->v ? -1 : 1;\n"
+        "  if (!xn && signbit(x->v) != signbit(y->v)) return signbit(x->v) ? 1 : -1;\n"),
+    "topk_pad_zero": ("for (int32_t t = m; t < k; ++t) o[t] = -1;",
+                      "for (int32_t t = m; t < k; ++t) o[t] = 0;"),
 }
 
 
