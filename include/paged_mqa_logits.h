@@ -131,6 +131,58 @@ int idx_paged_mqa_logits_bf16(const void* q, const void* kv_pages, const float* 
                               int64_t page_table_row_stride, hipStream_t stream);
 
 /*
+ * Top-k over logits rows: the selection the -inf-masked logits feed ("The
+ * Final Gate: Validating a Custom Triton Indexer Kernel Before Production
+ * Deployment", section "What the Test Output Reveals").  The pages give
+ * neither k nor a tie rule; this library's rule:
+ *
+ *   candidates  positions p < L_b of row b, L_b = clamp(seqlens[b], 0, ncols)
+ *   order       larger value first; equal values (+0 equals -0) by lower
+ *               position; NaN after every number
+ *   result      the first min(k, L_b) candidates of that order, written in
+ *               ascending position order to topk_idx[b][0..), then -1 up to k
+ *
+ *   logits      fp32 rows; row b starts at logits + b*row_stride (elements).
+ *               16-byte aligned, row_stride a multiple of 4 and >= ncols.
+ *               Only positions p < L_b are read.  May be NULL if ncols == 0.
+ *   seqlens     int32 [rows], 4-byte aligned.
+ *   rows, ncols, k   >= 0; rows == 0 or k == 0 returns IDX_OK with no launch.
+ *   topk_idx    int32 [rows][k], 4-byte aligned.
+ *   topk_val    optional (NULL: not written) fp32 [rows][k], 4-byte aligned:
+ *               the selected logits, bit for bit, and -inf for padding.
+ * One workgroup per row; the result is deterministic.
+ */
+int idx_topk_logits(const float* logits, int64_t row_stride, const int32_t* seqlens, int32_t rows,
+                    int32_t ncols, int32_t k, int32_t* topk_idx, float* topk_val,
+                    hipStream_t stream);
+
+/*
+ * Logits followed by their top-k, in one call on one stream: the arguments of
+ * idx_paged_mqa_logits_fp8 (q ... page_table_row_stride), then k, topk_idx and
+ * topk_val as in idx_topk_logits over the logits rows (ncols = row_stride =
+ * table_width*64).  `logits` is the caller's buffer [rows][table_width*64]
+ * for the intermediate scores.  Unlike idx_paged_mqa_logits_fp8 the -inf
+ * stores past each row's live pages are skipped where the kernel can skip
+ * them: after the call only positions p < L_b are defined, the rest hold
+ * their old contents or -inf.  Errors as both functions; nothing is launched
+ * on an error.
+ */
+int idx_paged_mqa_topk_fp8(const void* q, const void* kv_pages, const float* kscale,
+                           const int32_t* page_table, const int32_t* seqlens, const float* weights,
+                           float* logits, int32_t rows, int32_t num_heads, int32_t head_dim,
+                           int32_t table_width, int64_t num_pages, int64_t kv_page_stride,
+                           int64_t kscale_page_stride, int64_t page_table_row_stride, int32_t k,
+                           int32_t* topk_idx, float* topk_val, hipStream_t stream);
+
+/* bf16-key counterpart of idx_paged_mqa_topk_fp8 (kscale must be NULL). */
+int idx_paged_mqa_topk_bf16(const void* q, const void* kv_pages, const float* kscale,
+                            const int32_t* page_table, const int32_t* seqlens, const float* weights,
+                            float* logits, int32_t rows, int32_t num_heads, int32_t head_dim,
+                            int32_t table_width, int64_t num_pages, int64_t kv_page_stride,
+                            int64_t kscale_page_stride, int64_t page_table_row_stride, int32_t k,
+                            int32_t* topk_idx, float* topk_val, hipStream_t stream);
+
+/*
  * Paged key store, fp8: the write side of the cache block above.  Each of n
  * keys (128 values) is quantised and written to one slot of the pool.  The
  * pages give the block (64 positions x 128 fp8 values, then 64 fp32 scales;

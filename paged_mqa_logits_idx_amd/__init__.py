@@ -35,6 +35,9 @@ IDX_ERR_LAUNCH = -5
 _SYMBOLS = (
     "idx_paged_mqa_logits_fp8",
     "idx_paged_mqa_logits_bf16",
+    "idx_topk_logits",
+    "idx_paged_mqa_topk_fp8",
+    "idx_paged_mqa_topk_bf16",
     "idx_store_keys_fp8",
     "idx_store_keys_bf16",
     "idx_status_string",
@@ -64,6 +67,15 @@ def _load() -> ctypes.CDLL:
     for name in ("idx_paged_mqa_logits_fp8", "idx_paged_mqa_logits_bf16"):
         fn = getattr(lib, name)
         fn.argtypes = argtypes
+        fn.restype = ctypes.c_int
+    lib.idx_topk_logits.argtypes = [
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.idx_topk_logits.restype = ctypes.c_int
+    for name in ("idx_paged_mqa_topk_fp8", "idx_paged_mqa_topk_bf16"):
+        fn = getattr(lib, name)
+        fn.argtypes = argtypes[:-1] + [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p]
         fn.restype = ctypes.c_int
     lib.idx_store_keys_fp8.argtypes = [
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
@@ -177,6 +189,75 @@ def idx_paged_mqa_logits_bf16(q, kv_pages, kscale, page_table, seqlens, weights,
                  check=check)
 
 
+def idx_topk_logits(logits, seqlens, topk_idx, topk_val=None, *, k=None, rows=None, ncols=None,
+                    row_stride=None, stream=None, check=True) -> int:
+    """Per row b, the k largest of logits[b, :clamp(seqlens[b], 0, ncols)] (equal
+    values by lower position, NaN last), in ascending position order, -1 padded.
+
+    ``topk_idx`` int32 [rows, k]; ``topk_val`` optional fp32 [rows, k].  Dims
+    default to the tensors' shapes.
+    """
+    if isinstance(logits, torch.Tensor):
+        rows = logits.shape[0] if rows is None else rows
+        ncols = logits.shape[1] if ncols is None else ncols
+        row_stride = logits.stride(0) if row_stride is None else row_stride
+    if k is None:
+        k = topk_idx.shape[1]
+    dev = topk_idx.device if isinstance(topk_idx, torch.Tensor) else None
+    status = _lib.idx_topk_logits(_addr(logits), int(row_stride), _addr(seqlens), int(rows),
+                                  int(ncols), int(k), _addr(topk_idx), _addr(topk_val),
+                                  _stream_handle(stream, dev))
+    if check and status != IDX_OK:
+        raise IdxError(status, f"idx_topk_logits: {idx_status_string(status)}")
+    return status
+
+
+def _call_topk(name, q, kv_pages, kscale, page_table, seqlens, weights, logits, topk_idx, topk_val,
+               *, k, rows, num_heads, head_dim, table_width, num_pages, kv_page_stride,
+               kscale_page_stride, page_table_row_stride, stream, check):
+    rows, num_heads, head_dim, table_width, pts = _dims(
+        q, page_table, table_width, rows, num_heads, head_dim, page_table_row_stride)
+    if k is None:
+        k = topk_idx.shape[1]
+    dev = q.device if isinstance(q, torch.Tensor) else None
+    status = getattr(_lib, name)(
+        _addr(q), _addr(kv_pages), _addr(kscale), _addr(page_table), _addr(seqlens),
+        _addr(weights), _addr(logits), int(rows), int(num_heads), int(head_dim), int(table_width),
+        int(num_pages), int(kv_page_stride), int(kscale_page_stride), int(pts), int(k),
+        _addr(topk_idx), _addr(topk_val), _stream_handle(stream, dev))
+    if check and status != IDX_OK:
+        raise IdxError(status, f"{name}: {idx_status_string(status)}")
+    return status
+
+
+def idx_paged_mqa_topk_fp8(q, kv_pages, kscale, page_table, seqlens, weights, logits, topk_idx,
+                           topk_val=None, *, num_pages, k=None,
+                           kv_page_stride=FP8_FUSED_PAGE_BYTES,
+                           kscale_page_stride=FP8_FUSED_PAGE_BYTES, table_width=None,
+                           page_table_row_stride=None, rows=None, num_heads=None, head_dim=None,
+                           stream=None, check=True) -> int:
+    """Logits into ``logits`` (only positions p < seqlens[b] defined afterwards),
+    then their top-k into ``topk_idx`` / ``topk_val``, in one call."""
+    return _call_topk("idx_paged_mqa_topk_fp8", q, kv_pages, kscale, page_table, seqlens, weights,
+                      logits, topk_idx, topk_val, k=k, rows=rows, num_heads=num_heads,
+                      head_dim=head_dim, table_width=table_width, num_pages=num_pages,
+                      kv_page_stride=kv_page_stride, kscale_page_stride=kscale_page_stride,
+                      page_table_row_stride=page_table_row_stride, stream=stream, check=check)
+
+
+def idx_paged_mqa_topk_bf16(q, kv_pages, kscale, page_table, seqlens, weights, logits, topk_idx,
+                            topk_val=None, *, num_pages, k=None, kv_page_stride=BF16_PAGE_BYTES,
+                            kscale_page_stride=0, table_width=None, page_table_row_stride=None,
+                            rows=None, num_heads=None, head_dim=None, stream=None,
+                            check=True) -> int:
+    """bf16-key counterpart of :func:`idx_paged_mqa_topk_fp8` (kscale must be None)."""
+    return _call_topk("idx_paged_mqa_topk_bf16", q, kv_pages, kscale, page_table, seqlens, weights,
+                      logits, topk_idx, topk_val, k=k, rows=rows, num_heads=num_heads,
+                      head_dim=head_dim, table_width=table_width, num_pages=num_pages,
+                      kv_page_stride=kv_page_stride, kscale_page_stride=kscale_page_stride,
+                      page_table_row_stride=page_table_row_stride, stream=stream, check=check)
+
+
 def idx_store_keys_fp8(keys, slots, kv_pages, kscale, *, num_pages, n=None,
                        kv_page_stride=FP8_FUSED_PAGE_BYTES, kscale_page_stride=FP8_FUSED_PAGE_BYTES,
                        stream=None, check=True) -> int:
@@ -210,7 +291,8 @@ def idx_store_keys_bf16(keys, slots, kv_pages, *, num_pages, n=None, kv_page_str
 
 
 __all__ = [
-    "idx_paged_mqa_logits_fp8", "idx_paged_mqa_logits_bf16", "idx_store_keys_fp8",
+    "idx_paged_mqa_logits_fp8", "idx_paged_mqa_logits_bf16", "idx_topk_logits",
+    "idx_paged_mqa_topk_fp8", "idx_paged_mqa_topk_bf16", "idx_store_keys_fp8",
     "idx_store_keys_bf16", "idx_status_string",
     "idx_abi_version", "IdxError", "LIB_PATH", "NUM_HEADS", "HEAD_DIM", "PAGE_POSITIONS",
 ]

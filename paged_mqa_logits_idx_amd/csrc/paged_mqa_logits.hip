@@ -65,6 +65,7 @@ struct Params {
   float* out;         // [rows][width*64]
   int64_t num_pages, kv_stride, ks_stride, pt_stride;
   int32_t rows, width;
+  int32_t fill;       // 0: page slots past a row's live pages are left unwritten
 };
 
 // Raw key bytes of one page for one lane, already in B-fragment order:
@@ -323,7 +324,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(KEY 
         }
       }
     }
-    if (jl < jend) fill_neg_inf(orow, jl, jend - jl, lane);
+    if (p.fill && jl < jend) fill_neg_inf(orow, jl, jend - jl, lane);
   }
 }
 
@@ -687,13 +688,15 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(KEY 
   // Weighing the first half's live share 3:2 evens the finish (measured: the
   // 4097-wide decode 42.0 -> 41.2 us).
   const int64_t h = (int64_t)WAVES * ((gridDim.x + 1) / 2);  // first-half waves
-  const int64_t s = share_bound(wid, nw, h, 3, 2, total), e = share_bound(wid + 1, nw, h, 3, 2, total);
+  const int64_t wa = p.fill ? 3 : 1, wb = p.fill ? 2 : 1;     // no -inf share: even split
+  const int64_t s = share_bound(wid, nw, h, wa, wb, total), e = share_bound(wid + 1, nw, h, wa, wb, total);
   // (2) the -inf share: an equal share of the page slots.  Workgroups of the
   // grid's second half score first and write -inf after, those of the first
   // half the reverse.  The dispatcher gives every CU one workgroup of each
   // half, so each SIMD keeps one wave on the MFMA/VALU-heavy scoring while the
   // other streams stores, and HBM sees reads and writes together.
   FillCursor fc = fill_cursor(p, wid, nw);
+  if (!p.fill) fc.z = fc.a;  // nothing to write past the live pages
   if (2 * blockIdx.x >= gridDim.x) {
     if (s < e) live_share<KEY, NS>(p, s, e, lane, dma_slots + wave * NS * kSlotBytes);
     fill_rest(p, fc, lane);
@@ -930,7 +933,7 @@ __global__ __launch_bounds__(64 * kSharedRows) void shared_kernel(Params p, int3
       __builtin_amdgcn_s_waitcnt(wait_vm(0));
       __builtin_amdgcn_s_barrier();  // LDS is reused by this workgroup's next unit
     }
-    if (row_ok && jl < jend) fill_neg_inf(orow, jl, jend - jl, lane);
+    if (row_ok && p.fill && jl < jend) fill_neg_inf(orow, jl, jend - jl, lane);
   }
 }
 
@@ -1015,6 +1018,174 @@ __global__ __launch_bounds__(64 * kStoreWaves) void store_keys_kernel(const uint
 }
 
 // ---------------------------------------------------------------------------
+// Top-k over logits rows.  Candidates of row b are positions p < L_b; the
+// order is larger value first, equal values (+0 and -0 are equal) by lower
+// position, NaN after every number; the first min(k, L) candidates are
+// written in ascending position order, then -1 (value -inf) up to k.
+//
+// One workgroup per row.  A radix select over 32-bit order keys (digits of
+// 11, 11 and 10 bits, most significant first) finds the key T of the k-th
+// candidate and how many candidates with key T are taken (`need`; every key
+// above T is taken).  An order-preserving compaction then writes candidate p
+// to slot (#keys > T before p) + min(#keys == T before p, need).  Every pass
+// reads the row from memory (it is L2-resident after the logits kernel).
+constexpr int kTopkThreads = 1024;
+constexpr int kTopkWaves = kTopkThreads / 64;
+constexpr int kTopkBins = 2048;
+
+// Unsigned order equals the value order; -0 and +0 share a key; NaN gets 0,
+// below -inf (0x007fffff).
+__device__ __forceinline__ uint32_t order_key(float v) {
+  if (v != v) return 0u;
+  const uint32_t b = (v == 0.0f) ? 0u : __float_as_uint(v);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// Exclusive prefix sum over the workgroup's threads in thread order; `total`
+// receives the sum.  Every thread of the workgroup must call it.
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wave_sums, uint32_t& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t incl = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t t = __shfl_up(incl, d);
+    if (lane >= d) incl += t;
+  }
+  if (lane == 63) wave_sums[wave] = incl;
+  __syncthreads();
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kTopkWaves; ++w) {
+    const uint32_t s = wave_sums[w];
+    all += s;
+    before += (w < wave) ? s : 0u;
+  }
+  __syncthreads();  // wave_sums is rewritten by the next scan
+  total = all;
+  return before + incl - v;
+}
+
+// Four consecutive values starting at i (a multiple of 4); entries at or past
+// L are not read.
+__device__ __forceinline__ void load4(const float* x, int32_t i, int32_t L, float (&v)[4]) {
+  if (i + 4 <= L) {
+    const f32x4 t = *reinterpret_cast<const f32x4*>(x + i);
+    v[0] = t[0]; v[1] = t[1]; v[2] = t[2]; v[3] = t[3];
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = (i + e < L) ? x[i + e] : 0.0f;
+  }
+}
+
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* logits, int64_t row_stride,
+                                                            const int32_t* seqlens, int32_t rows,
+                                                            int32_t ncols, int32_t k, int32_t* idx_out,
+                                                            float* val_out) {
+  __shared__ uint32_t hist[kTopkBins];
+  __shared__ uint32_t wave_sums[kTopkWaves];
+  __shared__ uint32_t pick[2];  // chosen digit, candidates in the bins above it
+  const int tid = threadIdx.x;
+  for (int32_t b = blockIdx.x; b < rows; b += gridDim.x) {
+    const int32_t L = min(max(seqlens[b], 0), ncols);
+    const float* x = logits + (int64_t)b * row_stride;
+    int32_t* io = idx_out + (int64_t)b * k;
+    float* vo = val_out ? val_out + (int64_t)b * k : nullptr;
+    for (int32_t t = min(L, k) + tid; t < k; t += kTopkThreads) {
+      io[t] = -1;
+      if (vo) vo[t] = -INFINITY;
+    }
+    if (L <= k) {  // every candidate is selected
+      for (int32_t t = tid; t < L; t += kTopkThreads) {
+        io[t] = t;
+        if (vo) vo[t] = x[t];
+      }
+      continue;
+    }
+
+    // Radix select.  Invariant: 1 <= need <= #candidates whose key matches
+    // `prefix` on `mask`.
+    uint32_t prefix = 0u, mask = 0u, need = (uint32_t)k;
+    for (int pass = 0; pass < 3; ++pass) {
+      const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+      const uint32_t dmask = pass < 2 ? 0x7FFu : 0x3FFu;
+      for (int i = tid; i < kTopkBins; i += kTopkThreads) hist[i] = 0u;
+      __syncthreads();
+      for (int32_t i = 4 * tid; i < L; i += 4 * kTopkThreads) {
+        float v[4];
+        load4(x, i, L, v);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t key = order_key(v[e]);
+          if (i + e < L && (key & mask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1u);
+        }
+      }
+      __syncthreads();
+      // Bins in descending order: thread t holds bins 2047-2t and 2046-2t.
+      const int hi = kTopkBins - 1 - 2 * tid, lo = hi - 1;
+      const uint32_t chi = hist[hi], clo = hist[lo];
+      uint32_t total;
+      const uint32_t above = block_exclusive_scan(chi + clo, wave_sums, total);
+      if (above < need && need <= above + chi) {
+        pick[0] = (uint32_t)hi;
+        pick[1] = above;
+      } else if (above + chi < need && need <= above + chi + clo) {
+        pick[0] = (uint32_t)lo;
+        pick[1] = above + chi;
+      }
+      __syncthreads();
+      const uint32_t d = pick[0];
+      need -= pick[1];
+      const uint32_t in_bin = hist[d];
+      prefix |= d << shift;
+      mask |= dmask << shift;
+      __syncthreads();  // hist and pick are rewritten by the next pass
+      if (need == in_bin) break;  // the whole bin is taken: no finer digit needed
+    }
+
+    // Compaction in position order, 4 consecutive positions per thread.
+    uint32_t base_gt = 0u, base_eq = 0u;
+    for (int32_t c0 = 0; c0 < L; c0 += 4 * kTopkThreads) {
+      const int32_t i0 = c0 + 4 * tid;
+      float v[4];
+      uint32_t gt = 0u, eq = 0u;  // bit e: position i0+e is above / at the threshold
+      if (i0 < L) {
+        load4(x, i0, L, v);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t key = order_key(v[e]) & mask;
+          if (i0 + e < L) {
+            gt |= (key > prefix ? 1u : 0u) << e;
+            eq |= (key == prefix ? 1u : 0u) << e;
+          }
+        }
+      }
+      // counts per chunk are at most 4096: two 16-bit fields in one scan
+      uint32_t total;
+      const uint32_t ex = block_exclusive_scan(__builtin_popcount(gt) | (__builtin_popcount(eq) << 16),
+                                               wave_sums, total);
+      uint32_t g = base_gt + (ex & 0xFFFFu), q = base_eq + (ex >> 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if ((gt >> e) & 1u) {
+          const uint32_t slot = g + min(q, need);
+          io[slot] = i0 + e;
+          if (vo) vo[slot] = v[e];
+          ++g;
+        } else if ((eq >> e) & 1u) {
+          if (q < need) {
+            io[g + q] = i0 + e;
+            if (vo) vo[g + q] = v[e];
+          }
+          ++q;
+        }
+      }
+      base_gt += total & 0xFFFFu;
+      base_eq += total >> 16;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host side.
 
 constexpr int kRowwisePPW = 2;
@@ -1071,7 +1242,7 @@ int launch(const void* q, const void* kv_pages, const float* kscale, const int32
            const int32_t* seqlens, const float* weights, float* out, int32_t rows,
            int32_t num_heads, int32_t head_dim, int32_t table_width, int64_t num_pages,
            int64_t kv_page_stride, int64_t kscale_page_stride, int64_t page_table_row_stride,
-           hipStream_t stream) {
+           hipStream_t stream, bool fill = true) {
   const int st = validate(KEY, q, kv_pages, kscale, page_table, seqlens, weights, out, rows,
                           num_heads, head_dim, table_width, num_pages, kv_page_stride,
                           kscale_page_stride, page_table_row_stride);
@@ -1091,6 +1262,7 @@ int launch(const void* q, const void* kv_pages, const float* kscale, const int32
   p.pt_stride = page_table_row_stride;
   p.rows = rows;
   p.width = table_width;
+  p.fill = fill ? 1 : 0;
 
   (void)hipGetLastError();  // start from a clean error state
   if (page_table_row_stride != 0 || rows == 1) {
@@ -1126,6 +1298,54 @@ int launch(const void* q, const void* kv_pages, const float* kscale, const int32
     rowwise_kernel<KEY, kRowwisePPW, kRowwiseWaves>
         <<<dim3((uint32_t)grid), dim3(64 * kRowwiseWaves), 0, stream>>>(p, units_per_row, total);
   }
+  return hipGetLastError() == hipSuccess ? IDX_OK : IDX_ERR_LAUNCH;
+}
+
+int validate_topk(const float* logits, int64_t row_stride, const int32_t* seqlens, int32_t rows,
+                  int32_t ncols, int32_t k, const int32_t* topk_idx, const float* topk_val) {
+  if (rows < 0 || ncols < 0 || k < 0 || row_stride < ncols) return IDX_ERR_SHAPE;
+  if (rows == 0 || k == 0) return IDX_OK;
+  if ((ncols > 0 && !logits) || !seqlens || !topk_idx) return IDX_ERR_NULL;
+  if (!aligned(logits, 16) || (row_stride % 4) != 0 || !aligned(seqlens, 4) || !aligned(topk_idx, 4) ||
+      (topk_val && !aligned(topk_val, 4)))
+    return IDX_ERR_ALIGN;
+  return IDX_OK;
+}
+
+void launch_topk(const float* logits, int64_t row_stride, const int32_t* seqlens, int32_t rows,
+                 int32_t ncols, int32_t k, int32_t* topk_idx, float* topk_val, hipStream_t stream) {
+  const int64_t cap = (int64_t)16 * device_cu_count();
+  const int64_t grid = rows < cap ? rows : cap;
+  topk_kernel<<<dim3((uint32_t)grid), dim3(kTopkThreads), 0, stream>>>(logits, row_stride, seqlens, rows,
+                                                                       ncols, k, topk_idx, topk_val);
+}
+
+template <int KEY>
+int launch_logits_topk(const void* q, const void* kv_pages, const float* kscale, const int32_t* page_table,
+                       const int32_t* seqlens, const float* weights, float* logits, int32_t rows,
+                       int32_t num_heads, int32_t head_dim, int32_t table_width, int64_t num_pages,
+                       int64_t kv_page_stride, int64_t kscale_page_stride,
+                       int64_t page_table_row_stride, int32_t k, int32_t* topk_idx, float* topk_val,
+                       hipStream_t stream) {
+  const int st = validate(KEY, q, kv_pages, kscale, page_table, seqlens, weights, logits, rows, num_heads,
+                          head_dim, table_width, num_pages, kv_page_stride, kscale_page_stride,
+                          page_table_row_stride);
+  if (st != IDX_OK) return st;
+  const int64_t ncols = (int64_t)table_width * kPage;
+  const int st2 = validate_topk(logits, ncols, seqlens, rows, (int32_t)ncols, k, topk_idx, topk_val);
+  if (st2 != IDX_OK) return st2;
+  if (rows == 0) return IDX_OK;
+  if (table_width == 0) {  // no candidates: the top-k rows are all padding
+    if (k == 0) return IDX_OK;
+    (void)hipGetLastError();
+    launch_topk(logits, 0, seqlens, rows, 0, k, topk_idx, topk_val, stream);
+    return hipGetLastError() == hipSuccess ? IDX_OK : IDX_ERR_LAUNCH;
+  }
+  const int st3 = launch<KEY>(q, kv_pages, kscale, page_table, seqlens, weights, logits, rows, num_heads,
+                              head_dim, table_width, num_pages, kv_page_stride, kscale_page_stride,
+                              page_table_row_stride, stream, /*fill=*/false);
+  if (st3 != IDX_OK || k == 0) return st3;
+  launch_topk(logits, ncols, seqlens, rows, (int32_t)ncols, k, topk_idx, topk_val, stream);
   return hipGetLastError() == hipSuccess ? IDX_OK : IDX_ERR_LAUNCH;
 }
 
@@ -1179,6 +1399,39 @@ int idx_paged_mqa_logits_bf16(const void* q, const void* kv_pages, const float* 
   return launch<kBf16>(q, kv_pages, kscale, page_table, seqlens, weights, out, rows, num_heads,
                        head_dim, table_width, num_pages, kv_page_stride, kscale_page_stride,
                        page_table_row_stride, stream);
+}
+
+int idx_topk_logits(const float* logits, int64_t row_stride, const int32_t* seqlens, int32_t rows,
+                    int32_t ncols, int32_t k, int32_t* topk_idx, float* topk_val, hipStream_t stream) {
+  const int st = validate_topk(logits, row_stride, seqlens, rows, ncols, k, topk_idx, topk_val);
+  if (st != IDX_OK || rows == 0 || k == 0) return st;
+  (void)hipGetLastError();
+  launch_topk(logits, row_stride, seqlens, rows, ncols, k, topk_idx, topk_val, stream);
+  return hipGetLastError() == hipSuccess ? IDX_OK : IDX_ERR_LAUNCH;
+}
+
+int idx_paged_mqa_topk_fp8(const void* q, const void* kv_pages, const float* kscale,
+                           const int32_t* page_table, const int32_t* seqlens, const float* weights,
+                           float* logits, int32_t rows, int32_t num_heads, int32_t head_dim,
+                           int32_t table_width, int64_t num_pages, int64_t kv_page_stride,
+                           int64_t kscale_page_stride, int64_t page_table_row_stride, int32_t k,
+                           int32_t* topk_idx, float* topk_val, hipStream_t stream) {
+  return launch_logits_topk<kFp8>(q, kv_pages, kscale, page_table, seqlens, weights, logits, rows,
+                                  num_heads, head_dim, table_width, num_pages, kv_page_stride,
+                                  kscale_page_stride, page_table_row_stride, k, topk_idx, topk_val,
+                                  stream);
+}
+
+int idx_paged_mqa_topk_bf16(const void* q, const void* kv_pages, const float* kscale,
+                            const int32_t* page_table, const int32_t* seqlens, const float* weights,
+                            float* logits, int32_t rows, int32_t num_heads, int32_t head_dim,
+                            int32_t table_width, int64_t num_pages, int64_t kv_page_stride,
+                            int64_t kscale_page_stride, int64_t page_table_row_stride, int32_t k,
+                            int32_t* topk_idx, float* topk_val, hipStream_t stream) {
+  return launch_logits_topk<kBf16>(q, kv_pages, kscale, page_table, seqlens, weights, logits, rows,
+                                   num_heads, head_dim, table_width, num_pages, kv_page_stride,
+                                   kscale_page_stride, page_table_row_stride, k, topk_idx, topk_val,
+                                   stream);
 }
 
 int idx_store_keys_fp8(const void* keys, const int64_t* slots, int64_t n, void* kv_pages, float* kscale,

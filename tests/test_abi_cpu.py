@@ -39,6 +39,14 @@ def lib():
     l.idx_store_keys_bf16.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                       ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
     l.idx_store_keys_bf16.restype = ctypes.c_int
+    l.idx_topk_logits.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32,
+                                  ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                  ctypes.c_void_p]
+    l.idx_topk_logits.restype = ctypes.c_int
+    for name in ("idx_paged_mqa_topk_fp8", "idx_paged_mqa_topk_bf16"):
+        getattr(l, name).argtypes = args[:-1] + [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        getattr(l, name).restype = ctypes.c_int
     l.idx_status_string.restype = ctypes.c_char_p
     l.idx_status_string.argtypes = [ctypes.c_int]
     return l
@@ -47,7 +55,8 @@ def lib():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "idx_abi_version", "idx_paged_mqa_logits_bf16", "idx_paged_mqa_logits_fp8",
-        "idx_status_string", "idx_store_keys_bf16", "idx_store_keys_fp8"])
+        "idx_paged_mqa_topk_bf16", "idx_paged_mqa_topk_fp8", "idx_status_string",
+        "idx_store_keys_bf16", "idx_store_keys_fp8", "idx_topk_logits"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -152,3 +161,61 @@ SF, SB = "idx_store_keys_fp8", "idx_store_keys_bf16"
 ])
 def test_store_host_validation(lib, name, kw, status):
     assert _store(lib, name, **kw) == status
+
+
+def _topk(lib, **kw):
+    a = dict(logits=16, row_stride=64, sl=4, rows=1, ncols=64, k=8, idx=4, val=None)
+    a.update(kw)
+    return lib.idx_topk_logits(a["logits"], a["row_stride"], a["sl"], a["rows"], a["ncols"], a["k"],
+                               a["idx"], a["val"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(rows=-1), IDX_ERR_SHAPE),
+    (dict(ncols=-1), IDX_ERR_SHAPE),
+    (dict(k=-1), IDX_ERR_SHAPE),
+    (dict(row_stride=60), IDX_ERR_SHAPE),             # shorter than a row
+    (dict(rows=0, logits=None, sl=None, idx=None), IDX_OK),
+    (dict(k=0, logits=None, sl=None, idx=None), IDX_OK),
+    (dict(logits=None), IDX_ERR_NULL),
+    (dict(sl=None), IDX_ERR_NULL),
+    (dict(idx=None), IDX_ERR_NULL),
+    (dict(logits=20), IDX_ERR_ALIGN),
+    (dict(row_stride=66), IDX_ERR_ALIGN),
+    (dict(sl=2), IDX_ERR_ALIGN),
+    (dict(idx=6), IDX_ERR_ALIGN),
+    (dict(val=2), IDX_ERR_ALIGN),
+])
+def test_topk_host_validation(lib, kw, status):
+    assert _topk(lib, **kw) == status
+
+
+def _fused(lib, name, k=8, idx=4, val=None, **kw):
+    a = dict(q=16, kv=16, ks=16, pt=4, sl=4, w=16, out=16, rows=1, heads=64, dim=128, width=1,
+             num_pages=1, kv_stride=8448, ks_stride=8448, pt_stride=1)
+    if name.endswith("bf16"):
+        a.update(ks=None, kv_stride=16384, ks_stride=0)
+    a.update(kw)
+    return getattr(lib, name)(a["q"], a["kv"], a["ks"], a["pt"], a["sl"], a["w"], a["out"], a["rows"],
+                              a["heads"], a["dim"], a["width"], a["num_pages"], a["kv_stride"],
+                              a["ks_stride"], a["pt_stride"], k, idx, val, None)
+
+
+TF, TB = "idx_paged_mqa_topk_fp8", "idx_paged_mqa_topk_bf16"
+
+
+@pytest.mark.parametrize("name,kw,status", [
+    (TF, dict(heads=32), IDX_ERR_UNSUPPORTED),
+    (TF, dict(kv_stride=8191), IDX_ERR_SHAPE),
+    (TF, dict(k=-1), IDX_ERR_SHAPE),
+    (TB, dict(k=-1), IDX_ERR_SHAPE),
+    (TF, dict(rows=0, q=None, idx=None), IDX_OK),             # nothing to do
+    (TF, dict(q=None), IDX_ERR_NULL),
+    (TF, dict(idx=None), IDX_ERR_NULL),
+    (TB, dict(ks=16), IDX_ERR_NULL),
+    (TF, dict(out=4), IDX_ERR_ALIGN),
+    (TF, dict(idx=2), IDX_ERR_ALIGN),
+    (TB, dict(val=6), IDX_ERR_ALIGN),
+])
+def test_fused_topk_host_validation(lib, name, kw, status):
+    assert _fused(lib, name, **kw) == status

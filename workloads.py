@@ -287,3 +287,21 @@ def run_library(dw: DeviceWorkload, lib_module, stream=None, check: bool = True)
         dw.q, dw.kv, None, dw.page_table, dw.seqlens, dw.weights, dw.out, rows=wl.rows,
         table_width=wl.table_width, num_pages=wl.num_pages, kv_page_stride=wl.kv_stride,
         kscale_page_stride=0, page_table_row_stride=wl.pt_stride, stream=stream, check=check)
+
+
+def run_library_topk(dw: DeviceWorkload, lib_module, topk_idx, topk_val=None, stream=None,
+                     check: bool = True) -> int:
+    """Call the fused logits + top-k entry point of the workload's key kind; the
+    logits go to dw.out (defined only at positions below each row's length)."""
+    wl = dw.wl
+    if wl.key_kind == "fp8":
+        return lib_module.idx_paged_mqa_topk_fp8(
+            dw.q, dw.kv, dw.kscale_addr, dw.page_table, dw.seqlens, dw.weights, dw.out, topk_idx,
+            topk_val, rows=wl.rows, table_width=wl.table_width, num_pages=wl.num_pages,
+            kv_page_stride=wl.kv_stride, kscale_page_stride=wl.ks_stride,
+            page_table_row_stride=wl.pt_stride, stream=stream, check=check)
+    return lib_module.idx_paged_mqa_topk_bf16(
+        dw.q, dw.kv, None, dw.page_table, dw.seqlens, dw.weights, dw.out, topk_idx, topk_val,
+        rows=wl.rows, table_width=wl.table_width, num_pages=wl.num_pages,
+        kv_page_stride=wl.kv_stride, kscale_page_stride=0, page_table_row_stride=wl.pt_stride,
+        stream=stream, check=check)
