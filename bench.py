@@ -12,7 +12,10 @@ Prints ONE JSON line:
                  launch time (HIP events on the launch stream) vs 8 TB/s
   cpu_baseline   the CPU oracle timed on a bounded row sample of the same workload
   secondary      same measurements for the 128-page decode, the 513-slot control
-                 of the default workload, and the bf16 prefill (MFMA roofline)
+                 of the default workload, the bf16 prefill (MFMA roofline), the
+                 crossed variants (bf16-key decode, fp8-key prefill), the fused
+                 logits + top-2048 call (with the top-k kernel alone) on the
+                 default workload and the prefill, and the fp8 key store
 
 Inputs are synthetic and seeded (workloads.py).  Key pools and outputs are
 rotated over enough copies that one launch's bytes are gone from the 256 MB
@@ -39,6 +42,7 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 KERNEL_SOURCE = ROOT / "paged_mqa_logits_idx_amd" / "csrc" / "paged_mqa_logits.hip"
 TRAFFIC_FILE = ROOT / "profiles" / "traffic.json"
 ROTATE_BYTES = 1 << 30           # >= 4x the 256 MB last-level cache
+TOPK = 2048                      # indices kept per row by the fused top-k line
 
 
 def log(msg: str) -> None:
@@ -71,8 +75,12 @@ def algorithmic_work(wl):
     return reads, writes, flops
 
 
-def measure(cfg, steps: int, warmup: int):
-    """Time `steps` back-to-back library calls on one GPU."""
+def measure(cfg, steps: int, warmup: int, topk: int | None = None):
+    """Time `steps` back-to-back library calls on one GPU.
+
+    With `topk`, the call is the fused logits + top-k entry point (k = topk),
+    and the top-k kernel alone is timed as well over the logits it left.
+    """
     import torch
 
     import paged_mqa_logits_idx_amd as lib
@@ -98,34 +106,22 @@ def measure(cfg, steps: int, warmup: int):
                 d.ks = base.ks.clone()
                 d.kscale_addr = d.ks.data_ptr() + wl.ks_offset
         sets.append(d)
-    # Warm-up on a side stream, then capture the K timed steps in one HIP graph
-    # so that launches run back to back (no host submission gaps) and time its
-    # replay with HIP events on the stream it runs on.
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        for i in range(warmup):
+    if topk is None:
+        def step(i):
             W.run_library(sets[i % n_sets], lib)
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for i in range(steps):
-            W.run_library(sets[i % n_sets], lib)
-    graph.replay()  # untimed: first replay of the captured steps
-    torch.cuda.synchronize()
+    else:
+        idx = [torch.empty((wl.rows, topk), dtype=torch.int32, device="cuda") for _ in range(n_sets)]
 
-    stream = torch.cuda.current_stream()
-    region_s, region_e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    region_s.record(stream)
-    graph.replay()
-    region_e.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    region_ms = region_s.elapsed_time(region_e)
+        def step(i):
+            W.run_library_topk(sets[i % n_sets], lib, idx[i % n_sets])
+    region_ms, wall = time_graph(step, steps, warmup)
     mean_ms = region_ms / steps
+    topk_ms = None
+    if topk is not None:
+        def topk_step(i):
+            d = sets[i % n_sets]
+            lib.idx_topk_logits(d.out, d.seqlens, idx[i % n_sets])
+        topk_ms = time_graph(topk_step, steps, warmup)[0] / steps
     reads, writes, flops = algorithmic_work(wl)
     res = {
         "cfg": cfg, "name": wl.name, "rows": wl.rows, "table_width": wl.table_width,
@@ -136,10 +132,43 @@ def measure(cfg, steps: int, warmup: int):
         "gbs": (reads + writes) / (mean_ms * 1e-3) / 1e9,
         "tflops": flops / (mean_ms * 1e-3) / 1e12,
         "positions_per_s_kernel": wl.live_positions() / (mean_ms * 1e-3),
+        "shared_table": wl.pt_stride == 0, "topk": topk, "topk_only_ms": topk_ms,
     }
-    del graph, sets, base
+    del sets, base
     torch.cuda.empty_cache()
     return wl, res
+
+
+def time_graph(step, steps: int, warmup: int):
+    """Warm up on a side stream, capture `steps` calls of step(i) in one HIP
+    graph (launches run back to back, no host submission gaps) and time one
+    replay with HIP events on the stream it runs on.  Returns (ms, wall s)."""
+    import torch
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(warmup):
+            step(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(steps):
+            step(i)
+    graph.replay()  # untimed: first replay of the captured steps
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    a.record(stream)
+    graph.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = a.elapsed_time(b)
+    del graph
+    return ms, wall
 
 
 def measure_store(steps: int, warmup: int):
@@ -167,28 +196,10 @@ def measure_store(steps: int, warmup: int):
         lib.idx_store_keys_fp8(keys, slots, pool, pool.data_ptr() + W.FP8_KEY_BYTES,
                                num_pages=num_pages)
 
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        for i in range(warmup):
-            step(i)
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for i in range(steps):
-            step(i)
-    graph.replay()
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    graph.replay()
-    b.record()
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / steps
+    ms = time_graph(step, steps, warmup)[0] / steps
     per_key = W.HEAD_DIM * 2 + 8 + W.HEAD_DIM + 4  # bf16 key + slot id in, codes + scale out
     alg = n * per_key
-    del graph, pools, keys, slots
+    del pools, keys, slots
     torch.cuda.empty_cache()
     return {"workload": f"fp8 key store, {n} keys into a {num_pages}-page pool (whole pages)",
             "kernel_ms_mean": round(ms, 5), "keys_per_s": n / (ms * 1e-3), "bound": "hbm",
@@ -279,7 +290,7 @@ def main() -> int:
 
     secondary = {}
     if not args.no_secondary:
-        for c in (2, "3c", 4):
+        for c in (2, "3c", 4, "2b", "4f"):
             if str(c) == str(cfg):
                 continue
             _, r = measure(c, max(10, args.steps // 2), max(3, args.warmup // 2))
@@ -288,7 +299,7 @@ def main() -> int:
                 "workload": r["name"], "kernel_ms_mean": round(r["kernel_ms_mean"], 5),
                 "positions_per_s": r["positions_per_s_kernel"],
             }
-            if r["key_kind"] == "bf16":
+            if r["shared_table"]:  # prefill: one key read serves many rows
                 entry.update(bound="mfma", achieved_tflops=round(r["tflops"], 2),
                              peak_tflops=BF16_MFMA_PEAK_TFLOPS,
                              frac=round(r["tflops"] / BF16_MFMA_PEAK_TFLOPS, 4),
@@ -298,6 +309,15 @@ def main() -> int:
                              frac=round(r["gbs"] / HBM_PEAK_GBS, 4),
                              alg_bytes=r["alg_read_bytes"] + r["alg_write_bytes"])
             secondary[str(c)] = entry
+        for c in (cfg, 4):
+            _, r = measure(c, max(10, args.steps // 2), max(3, args.warmup // 2), topk=TOPK)
+            log(json.dumps(r))
+            secondary[f"topk_{c}"] = {
+                "workload": f"{r['name']}, logits + top-{TOPK} (fused call, no -inf tail)",
+                "k": TOPK, "kernel_ms_mean": round(r["kernel_ms_mean"], 5),
+                "topk_only_ms": round(r["topk_only_ms"], 5),
+                "positions_per_s": r["positions_per_s_kernel"],
+            }
         r = measure_store(max(10, args.steps // 2), max(3, args.warmup // 2))
         log(json.dumps(r))
         secondary["store_fp8"] = r

@@ -1027,11 +1027,25 @@ __global__ __launch_bounds__(64 * kStoreWaves) void store_keys_kernel(const uint
 // 11, 11 and 10 bits, most significant first) finds the key T of the k-th
 // candidate and how many candidates with key T are taken (`need`; every key
 // above T is taken).  An order-preserving compaction then writes candidate p
-// to slot (#keys > T before p) + min(#keys == T before p, need).  Every pass
-// reads the row from memory (it is L2-resident after the logits kernel).
-constexpr int kTopkThreads = 1024;
-constexpr int kTopkWaves = kTopkThreads / 64;
+// to slot (#keys > T before p) + min(#keys == T before p, need): each wave
+// owns a contiguous segment of the row, 4 positions per lane and 256 per
+// step, counts its candidates with ballots and emits them after a prefix
+// over the waves' counts.
+// A row of at most CAP candidates is staged once in LDS (by DMA) and every
+// pass reads it there; after the first digit, the keys that share it (at
+// most CAND of them) are gathered into a list that the later digits scan
+// instead of the row.  A longer row is re-read from memory by each pass.
 constexpr int kTopkBins = 2048;
+
+template <int THREADS, int CAP, int CAND>
+struct TopkShared {
+  float vals[CAP];       // the row, when it fits
+  uint32_t cand[CAND];   // keys sharing the first digit
+  uint32_t hist[kTopkBins];
+  uint32_t wave_gt[THREADS / 64], wave_eq[THREADS / 64];
+  uint32_t pick[3];      // chosen digit, candidates in the digits above it, in it
+  uint32_t ncand;
+};
 
 // Unsigned order equals the value order; -0 and +0 share a key; NaN gets 0,
 // below -inf (0x007fffff).
@@ -1041,29 +1055,22 @@ __device__ __forceinline__ uint32_t order_key(float v) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// Exclusive prefix sum over the workgroup's threads in thread order; `total`
-// receives the sum.  Every thread of the workgroup must call it.
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wave_sums, uint32_t& total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t incl = v;
+__device__ __forceinline__ uint32_t wave_inclusive_scan_u32(uint32_t v, int lane) {
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t t = __shfl_up(incl, d);
-    if (lane >= d) incl += t;
+    const uint32_t t = __shfl_up(v, d);
+    if (lane >= d) v += t;
   }
-  if (lane == 63) wave_sums[wave] = incl;
-  __syncthreads();
-  uint32_t before = 0, all = 0;
-#pragma unroll
-  for (int w = 0; w < kTopkWaves; ++w) {
-    const uint32_t s = wave_sums[w];
-    all += s;
-    before += (w < wave) ? s : 0u;
-  }
-  __syncthreads();  // wave_sums is rewritten by the next scan
-  total = all;
-  return before + incl - v;
+  return v;
 }
+
+// Set bits of a wave mask below this lane.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+__device__ __forceinline__ int topk_shift(int pass) { return pass == 0 ? 21 : (pass == 1 ? 10 : 0); }
+__device__ __forceinline__ uint32_t topk_dmask(int pass) { return pass < 2 ? 0x7FFu : 0x3FFu; }
 
 // Four consecutive values starting at i (a multiple of 4); entries at or past
 // L are not read.
@@ -1077,110 +1084,258 @@ __device__ __forceinline__ void load4(const float* x, int32_t i, int32_t L, floa
   }
 }
 
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* logits, int64_t row_stride,
-                                                            const int32_t* seqlens, int32_t rows,
-                                                            int32_t ncols, int32_t k, int32_t* idx_out,
-                                                            float* val_out) {
-  __shared__ uint32_t hist[kTopkBins];
-  __shared__ uint32_t wave_sums[kTopkWaves];
-  __shared__ uint32_t pick[2];  // chosen digit, candidates in the bins above it
+template <bool RES, typename SH>
+__device__ __forceinline__ void row4(const SH& sh, const float* x, int32_t i, int32_t L, float (&v)[4]) {
+  if constexpr (RES) {
+    if (i + 4 <= L) {
+      const f32x4 t = *reinterpret_cast<const f32x4*>(&sh.vals[i]);
+      v[0] = t[0]; v[1] = t[1]; v[2] = t[2]; v[3] = t[3];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (i + e < L) ? sh.vals[i + e] : 0.0f;
+    }
+  } else {
+    load4(x, i, L, v);
+  }
+}
+
+// Wave 0, once sh.hist holds this digit's counts over the candidates that
+// match (prefix, mask): pick the digit holding the need-th largest of them,
+// with the counts above it and in it, and clear the histogram.  Two levels:
+// lane l sums digits 2047-32l down to 2016-32l and a scan finds the lane
+// whose range holds the pick; then lanes 0..31 take that range's digits in
+// descending order and a second scan finds the digit.
+template <typename SH>
+__device__ __forceinline__ void pick_digit(SH& sh, uint32_t need, int lane) {
+  const int lo = kTopkBins - 32 * (lane + 1);  // lowest digit of the lane
+  uint32_t sum = 0u;
+#pragma unroll
+  for (int i = 0; i < 32; i += 4) {
+    const u32x4 t = *reinterpret_cast<const u32x4*>(&sh.hist[lo + i]);
+    sum += t[0] + t[1] + t[2] + t[3];
+  }
+  const uint32_t incl = wave_inclusive_scan_u32(sum, lane);
+  const uint64_t hit = __ballot(incl - sum < need && need <= incl);  // exactly one lane
+  const int l1 = __builtin_amdgcn_readfirstlane(hit ? (int)__builtin_ctzll(hit) : 0);
+  const uint32_t above1 = __builtin_amdgcn_readlane(incl - sum, l1);
+  const int dg = kTopkBins - 1 - 32 * l1 - lane;  // lanes 0..31: the range, descending
+  const uint32_t c = lane < 32 ? sh.hist[dg] : 0u;
+  const uint32_t incl2 = above1 + wave_inclusive_scan_u32(c, lane);
+  if (lane < 32 && incl2 - c < need && need <= incl2) {  // exactly one lane
+    sh.pick[0] = (uint32_t)dg;
+    sh.pick[1] = incl2 - c;
+    sh.pick[2] = c;
+  }
+#pragma unroll
+  for (int i = 0; i < 32; i += 4) *reinterpret_cast<u32x4*>(&sh.hist[lo + i]) = (u32x4){0u, 0u, 0u, 0u};
+}
+
+// After a histogram: pick the digit, fold it into (prefix, mask), take the
+// candidates of the larger digits off `need`.  Returns the candidates in the
+// picked digit.  Every thread calls it.
+template <typename SH>
+__device__ __forceinline__ uint32_t radix_step(SH& sh, int pass, uint32_t& prefix, uint32_t& mask,
+                                               uint32_t& need, int wave, int lane) {
+  __syncthreads();  // the histogram is complete
+  if (wave == 0) pick_digit(sh, need, lane);
+  __syncthreads();  // (pick is next written after the next histogram's barrier)
+  need -= sh.pick[1];
+  prefix |= sh.pick[0] << topk_shift(pass);
+  mask |= topk_dmask(pass) << topk_shift(pass);
+  return sh.pick[2];
+}
+
+// Histogram of one digit over the row's keys that match (prefix, mask).
+template <bool RES, int THREADS, int STEPS, typename SH>
+__device__ __forceinline__ void row_histogram(SH& sh, const float* x, int32_t L, int pass, uint32_t prefix,
+                                              uint32_t mask) {
+  const int shift = topk_shift(pass);
+  const uint32_t dmask = topk_dmask(pass);
+  auto count4 = [&](int32_t i) {
+    float v[4];
+    row4<RES>(sh, x, i, L, v);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t key = order_key(v[e]);
+      if (i + e < L && (key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & dmask], 1u);
+    }
+  };
   const int tid = threadIdx.x;
+  if constexpr (RES) {
+#pragma unroll
+    for (int j = 0; j < STEPS; ++j) {  // STEPS 16-byte groups per thread cover the staged row
+      const int32_t i = 4 * THREADS * j + 4 * tid;
+      if (i < L) count4(i);
+    }
+  } else {
+    for (int32_t i = 4 * tid; i < L; i += 4 * THREADS) count4(i);
+  }
+}
+
+// Row of L > k candidates.  RES: the row is in sh.vals (L <= CAP).
+template <bool RES, int THREADS, int CAP, int CAND>
+__device__ __forceinline__ void topk_row(TopkShared<THREADS, CAP, CAND>& sh, const float* x, int32_t L,
+                                         int32_t k, int32_t* io, float* vo) {
+  constexpr int kWaves = THREADS / 64;
+  constexpr int kSteps = (CAP + 4 * THREADS - 1) / (4 * THREADS);  // staged 16-byte groups per thread
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // Radix select.  Invariant: 1 <= need <= candidates matching (prefix, mask).
+  uint32_t prefix = 0u, mask = 0u, need = (uint32_t)k;
+  row_histogram<RES, THREADS, kSteps>(sh, x, L, 0, prefix, mask);
+  uint32_t in_digit = radix_step(sh, 0, prefix, mask, need, wave, lane);
+  if (need != in_digit) {
+    // Gather the keys of the first digit (RES rows whose digit fits the list).
+    const bool listed = RES && in_digit <= (uint32_t)CAND;
+    if (listed) {
+      uint32_t hits = 0u, m = 0u;  // bit 4j+e: element (j, e) of this thread matches
+#pragma unroll
+      for (int j = 0; j < kSteps; ++j) {
+        const int32_t i = 4 * THREADS * j + 4 * tid;
+        if (i < L) {
+          float v[4];
+          row4<true>(sh, x, i, L, v);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bool hit = i + e < L && (order_key(v[e]) & mask) == prefix;
+            hits |= (hit ? 1u : 0u) << (4 * j + e);
+          }
+        }
+      }
+      m = __builtin_popcount(hits);
+      const uint32_t incl = wave_inclusive_scan_u32(m, lane);
+      uint32_t base = 0u;
+      if (lane == 63) base = atomicAdd(&sh.ncand, incl);
+      uint32_t at = __shfl(base, 63) + incl - m;
+#pragma unroll
+      for (int j = 0; j < kSteps; ++j) {
+        if ((hits >> (4 * j)) & 0xFu) {
+          const int32_t i = 4 * THREADS * j + 4 * tid;
+          float v[4];
+          row4<true>(sh, x, i, L, v);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if ((hits >> (4 * j + e)) & 1u) sh.cand[at++] = order_key(v[e]);
+        }
+      }
+      __syncthreads();
+    }
+    for (int pass = 1; pass < 3; ++pass) {
+      if (listed) {
+        const int shift = topk_shift(pass);
+        const uint32_t dmask = topk_dmask(pass);
+        for (int32_t i = tid; i < (int32_t)in_digit; i += THREADS) {
+          const uint32_t key = sh.cand[i];  // in_digit == the list's length
+          if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & dmask], 1u);
+        }
+      } else {
+        row_histogram<RES, THREADS, kSteps>(sh, x, L, pass, prefix, mask);
+      }
+      const uint32_t in_d = radix_step(sh, pass, prefix, mask, need, wave, lane);
+      if (need == in_d) break;  // the whole digit is taken: no finer digit needed
+    }
+  }
+
+  // Compaction: wave w owns positions [w*seg, (w+1)*seg), seg a multiple of
+  // 256; lane l holds positions c0+4l .. c0+4l+3 of each 256-position step.
+  const int32_t seg = ((L + kWaves - 1) / kWaves + 255) & ~255;
+  const int32_t s0 = min(wave * seg, L), s1 = min(s0 + seg, L);
+  uint32_t ng = 0u, nq = 0u;
+  for (int32_t c0 = s0; c0 < s1; c0 += 256) {
+    float v[4];
+    row4<RES>(sh, x, c0 + 4 * lane, s1, v);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool ok = c0 + 4 * lane + e < s1;
+      const uint32_t key = order_key(v[e]) & mask;
+      ng += (uint32_t)__builtin_popcountll(__ballot(ok && key > prefix));
+      nq += (uint32_t)__builtin_popcountll(__ballot(ok && key == prefix));
+    }
+  }
+  if (lane == 0) {
+    sh.wave_gt[wave] = ng;
+    sh.wave_eq[wave] = nq;
+  }
+  __syncthreads();
+  uint32_t g = 0u, q = 0u;
+  for (int w = 0; w < wave; ++w) {
+    g += sh.wave_gt[w];
+    q += sh.wave_eq[w];
+  }
+  for (int32_t c0 = s0; c0 < s1; c0 += 256) {
+    float v[4];
+    row4<RES>(sh, x, c0 + 4 * lane, s1, v);
+    bool gt[4], eq[4];
+    uint64_t bg[4], be[4];
+    uint32_t gl = g, ql = q;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool ok = c0 + 4 * lane + e < s1;
+      const uint32_t key = order_key(v[e]) & mask;
+      gt[e] = ok && key > prefix;
+      eq[e] = ok && key == prefix;
+      bg[e] = __ballot(gt[e]);
+      be[e] = __ballot(eq[e]);
+      gl += lanes_below(bg[e]);
+      ql += lanes_below(be[e]);
+      g += (uint32_t)__builtin_popcountll(bg[e]);
+      q += (uint32_t)__builtin_popcountll(be[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t slot = gl + min(ql, need);  // a key at the threshold: gl + ql when taken
+      if (gt[e] || (eq[e] && ql < need)) {
+        io[slot] = c0 + 4 * lane + e;
+        if (vo) vo[slot] = v[e];
+      }
+      gl += gt[e] ? 1u : 0u;
+      ql += eq[e] ? 1u : 0u;
+    }
+  }
+  __syncthreads();  // wave_gt / wave_eq / vals / cand are rewritten by the next row
+}
+
+template <int THREADS, int CAP, int CAND>
+__global__ __launch_bounds__(THREADS) void topk_kernel(const float* logits, int64_t row_stride,
+                                                       const int32_t* seqlens, int32_t rows, int32_t ncols,
+                                                       int32_t k, int32_t* idx_out, float* val_out) {
+  __shared__ __attribute__((aligned(16))) TopkShared<THREADS, CAP, CAND> sh;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kTopkBins; i += THREADS) sh.hist[i] = 0u;  // wave 0 re-clears after each pick
   for (int32_t b = blockIdx.x; b < rows; b += gridDim.x) {
     const int32_t L = min(max(seqlens[b], 0), ncols);
     const float* x = logits + (int64_t)b * row_stride;
     int32_t* io = idx_out + (int64_t)b * k;
     float* vo = val_out ? val_out + (int64_t)b * k : nullptr;
-    for (int32_t t = min(L, k) + tid; t < k; t += kTopkThreads) {
+    for (int32_t t = min(L, k) + tid; t < k; t += THREADS) {
       io[t] = -1;
       if (vo) vo[t] = -INFINITY;
     }
+    if (tid == 0) sh.ncand = 0u;
     if (L <= k) {  // every candidate is selected
-      for (int32_t t = tid; t < L; t += kTopkThreads) {
+      for (int32_t t = tid; t < L; t += THREADS) {
         io[t] = t;
         if (vo) vo[t] = x[t];
       }
-      continue;
-    }
-
-    // Radix select.  Invariant: 1 <= need <= #candidates whose key matches
-    // `prefix` on `mask`.
-    uint32_t prefix = 0u, mask = 0u, need = (uint32_t)k;
-    for (int pass = 0; pass < 3; ++pass) {
-      const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-      const uint32_t dmask = pass < 2 ? 0x7FFu : 0x3FFu;
-      for (int i = tid; i < kTopkBins; i += kTopkThreads) hist[i] = 0u;
-      __syncthreads();
-      for (int32_t i = 4 * tid; i < L; i += 4 * kTopkThreads) {
-        float v[4];
-        load4(x, i, L, v);
+    } else if (L <= CAP) {
+      // Stage the row in LDS by DMA (16 bytes per lane, lane-linear within
+      // the wave's 1 KiB), all of it in flight at once; the last L % 4 values
+      // by thread 0.
+      const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t key = order_key(v[e]);
-          if (i + e < L && (key & mask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1u);
-        }
+      for (int j = 0; j < (CAP + 4 * THREADS - 1) / (4 * THREADS); ++j) {
+        const int32_t i = 4 * THREADS * j + 4 * tid;
+        if (i + 4 <= L)
+          __builtin_amdgcn_global_load_lds((global_ptr)(x + i),
+                                           (lds_ptr)(&sh.vals[4 * THREADS * j + 256 * wave]), 16, 0, 0);
       }
+      if (tid == 0)
+        for (int32_t i = L & ~3; i < L; ++i) sh.vals[i] = x[i];
+      __builtin_amdgcn_s_waitcnt(wait_vm(0));  // the DMAs are not covered by the compiler's waits
       __syncthreads();
-      // Bins in descending order: thread t holds bins 2047-2t and 2046-2t.
-      const int hi = kTopkBins - 1 - 2 * tid, lo = hi - 1;
-      const uint32_t chi = hist[hi], clo = hist[lo];
-      uint32_t total;
-      const uint32_t above = block_exclusive_scan(chi + clo, wave_sums, total);
-      if (above < need && need <= above + chi) {
-        pick[0] = (uint32_t)hi;
-        pick[1] = above;
-      } else if (above + chi < need && need <= above + chi + clo) {
-        pick[0] = (uint32_t)lo;
-        pick[1] = above + chi;
-      }
+      topk_row<true>(sh, x, L, k, io, vo);
+    } else {
       __syncthreads();
-      const uint32_t d = pick[0];
-      need -= pick[1];
-      const uint32_t in_bin = hist[d];
-      prefix |= d << shift;
-      mask |= dmask << shift;
-      __syncthreads();  // hist and pick are rewritten by the next pass
-      if (need == in_bin) break;  // the whole bin is taken: no finer digit needed
-    }
-
-    // Compaction in position order, 4 consecutive positions per thread.
-    uint32_t base_gt = 0u, base_eq = 0u;
-    for (int32_t c0 = 0; c0 < L; c0 += 4 * kTopkThreads) {
-      const int32_t i0 = c0 + 4 * tid;
-      float v[4];
-      uint32_t gt = 0u, eq = 0u;  // bit e: position i0+e is above / at the threshold
-      if (i0 < L) {
-        load4(x, i0, L, v);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t key = order_key(v[e]) & mask;
-          if (i0 + e < L) {
-            gt |= (key > prefix ? 1u : 0u) << e;
-            eq |= (key == prefix ? 1u : 0u) << e;
-          }
-        }
-      }
-      // counts per chunk are at most 4096: two 16-bit fields in one scan
-      uint32_t total;
-      const uint32_t ex = block_exclusive_scan(__builtin_popcount(gt) | (__builtin_popcount(eq) << 16),
-                                               wave_sums, total);
-      uint32_t g = base_gt + (ex & 0xFFFFu), q = base_eq + (ex >> 16);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if ((gt >> e) & 1u) {
-          const uint32_t slot = g + min(q, need);
-          io[slot] = i0 + e;
-          if (vo) vo[slot] = v[e];
-          ++g;
-        } else if ((eq >> e) & 1u) {
-          if (q < need) {
-            io[g + q] = i0 + e;
-            if (vo) vo[g + q] = v[e];
-          }
-          ++q;
-        }
-      }
-      base_gt += total & 0xFFFFu;
-      base_eq += total >> 16;
+      topk_row<false>(sh, x, L, k, io, vo);
     }
   }
 }
@@ -1312,12 +1467,22 @@ int validate_topk(const float* logits, int64_t row_stride, const int32_t* seqlen
   return IDX_OK;
 }
 
+// Rows of at most 6144 candidates (ncols bounds every L) take 256-thread
+// workgroups staging up to 6144 values (four fit one CU's LDS); longer ones
+// 1024 threads staging up to 32768.
 void launch_topk(const float* logits, int64_t row_stride, const int32_t* seqlens, int32_t rows,
                  int32_t ncols, int32_t k, int32_t* topk_idx, float* topk_val, hipStream_t stream) {
-  const int64_t cap = (int64_t)16 * device_cu_count();
-  const int64_t grid = rows < cap ? rows : cap;
-  topk_kernel<<<dim3((uint32_t)grid), dim3(kTopkThreads), 0, stream>>>(logits, row_stride, seqlens, rows,
-                                                                       ncols, k, topk_idx, topk_val);
+  if (ncols <= 6144) {
+    const int64_t cap = (int64_t)64 * device_cu_count();
+    const int64_t grid = rows < cap ? rows : cap;
+    topk_kernel<256, 6144, 1024><<<dim3((uint32_t)grid), dim3(256), 0, stream>>>(
+        logits, row_stride, seqlens, rows, ncols, k, topk_idx, topk_val);
+  } else {
+    const int64_t cap = (int64_t)16 * device_cu_count();
+    const int64_t grid = rows < cap ? rows : cap;
+    topk_kernel<1024, 32768, 4096><<<dim3((uint32_t)grid), dim3(1024), 0, stream>>>(
+        logits, row_stride, seqlens, rows, ncols, k, topk_idx, topk_val);
+  }
 }
 
 template <int KEY>

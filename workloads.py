@@ -150,12 +150,17 @@ CONFIG_NAMES = {
     3: "fp8 decode O(actual) B=64 width=4097",
     "3c": "fp8 decode B=64 width=513 (same rows as width=4097)",
     4: "bf16 prefill T=4096 width=88",
+    "2b": "bf16-key decode B=64 width=128",
+    "4f": "fp8-key prefill T=4096 width=88",
 }
 
 
 def config(idx, layout: str = "fused") -> Workload:
-    """Seeded workload of one configuration (0-4, or "3c": config 3's data in a 513-slot table)."""
-    base = 3 if idx == "3c" else int(idx)
+    """Seeded workload of one configuration: 0-4; "3c" = the 4097-wide decode's
+    rows in a 513-slot table; "2b" / "4f" = the 128-page decode with bf16 keys /
+    the prefill with fp8 keys (same shapes, lengths and tables)."""
+    base = {"3c": 3, "2b": 2, "4f": 4}.get(idx, idx)
+    base = int(base)
     rng = np.random.Generator(np.random.PCG64(1000 + base))
     if base == 0:
         rows, width, pool, kind = 1, 8, 8, "fp8"
@@ -169,6 +174,8 @@ def config(idx, layout: str = "fused") -> Workload:
         rows, width, pool, kind = 4096, 88, 88, "bf16"
     else:
         raise ValueError(idx)
+    if idx in ("2b", "4f"):
+        kind = "bf16" if idx == "2b" else "fp8"
     q, w = draw_q_w(rng, rows)
     kv, kv_stride, ks, ks_off, ks_stride = keys_from_normal(rng, pool, kind, layout)
 
