@@ -47,7 +47,8 @@ class Oracle:
         P = ctypes.c_void_p
         lib.oracle_paged_mqa_logits.argtypes = [
             ctypes.c_int, P, P, ctypes.c_int64, P, ctypes.c_int64, ctypes.c_int64, P,
-            ctypes.c_int64, P, P, ctypes.c_int32, ctypes.c_int32, P, ctypes.c_int32, P]
+            ctypes.c_int64, P, ctypes.c_int32, P, P, ctypes.c_int32, ctypes.c_int32, P,
+            ctypes.c_int32, P]
         lib.oracle_paged_mqa_logits.restype = None
         lib.oracle_e4m3fn_encode.argtypes = [ctypes.c_float]
         lib.oracle_e4m3fn_encode.restype = ctypes.c_uint32
@@ -109,7 +110,8 @@ class Oracle:
         """float64 logits [len(rows) or wl.rows, table_width*64] of a workload.
 
         ``wl`` carries host arrays laid out as the library's arguments (see
-        workloads.Workload).  ``rows``: optional row indices to evaluate.
+        workloads.Workload; ``row_table`` / ``num_tables`` map rows to page
+        tables in a multi-request batch).  ``rows``: optional row indices.
         """
         kind = {"fp8": 0, "bf16": 1}[wl.key_kind]
         q = np.ascontiguousarray(wl.q, dtype=np.uint16)
@@ -119,6 +121,9 @@ class Oracle:
             ks = kv if wl.ks is wl.kv else np.ascontiguousarray(wl.ks, dtype=np.uint8)
             ks_addr = ks.ctypes.data + int(wl.ks_offset)
         pt = np.ascontiguousarray(wl.page_table, dtype=np.int32)
+        rt = getattr(wl, "row_table", None)
+        if rt is not None:
+            rt = np.ascontiguousarray(rt, dtype=np.int32)
         sl = np.ascontiguousarray(wl.seqlens, dtype=np.int32)
         w = np.ascontiguousarray(wl.weights, dtype=np.float32)
         if rows is None:
@@ -133,6 +138,7 @@ class Oracle:
             self.lib.oracle_paged_mqa_logits(
                 kind, q.ctypes.data, kv.ctypes.data, int(wl.kv_stride), ks_addr,
                 int(wl.ks_stride), int(wl.num_pages), pt.ctypes.data, int(wl.pt_stride),
+                None if rt is None else rt.ctypes.data, int(getattr(wl, "num_tables", 0)),
                 sl.ctypes.data, w.ctypes.data, int(wl.rows), int(wl.table_width),
                 None if row_ids is None else row_ids.ctypes.data, n_out, out.ctypes.data)
         return out

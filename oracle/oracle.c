@@ -79,7 +79,12 @@ enum { NH = 64, HD = 128, PG = 64 };
  *   q_bits      bf16 bits [rows][64][128]
  *   kv          key pool bytes; page g at kv + g*kv_stride
  *   ks          scale bytes (fp8 only); scale (g, i) at ks + g*ks_stride + 4*i
- *   page_table  int32; row b's table at page_table + b*pt_stride
+ *   page_table  int32; row b's table at page_table + t*pt_stride with
+ *               t = row_table[b] (a request's table; its rows are that
+ *               request's query tokens), or t = b when row_table is NULL
+ *   row_table   NULL, or int32 [rows]: table index of each row, valid in
+ *               [0, num_tables); a row with an index outside it scores NaN at
+ *               its live positions (as an invalid page id does)
  *   seqlens     int32 [rows]
  *   weights     fp32 [rows][64]
  *   row_ids     rows to evaluate (n_out of them); NULL = all rows in order
@@ -88,6 +93,7 @@ enum { NH = 64, HD = 128, PG = 64 };
 void oracle_paged_mqa_logits(int key_kind, const uint16_t* q_bits, const uint8_t* kv,
                              int64_t kv_stride, const uint8_t* ks, int64_t ks_stride,
                              int64_t num_pages, const int32_t* page_table, int64_t pt_stride,
+                             const int32_t* row_table, int32_t num_tables,
                              const int32_t* seqlens, const float* weights, int32_t rows,
                              int32_t table_width, const int32_t* row_ids, int32_t n_out,
                              double* out) {
@@ -110,7 +116,9 @@ void oracle_paged_mqa_logits(int key_kind, const uint16_t* q_bits, const uint8_t
       for (int i = 0; i < PG; ++i) o[i] = -INFINITY;
       continue;
     }
-    const int32_t g = page_table[(int64_t)b * pt_stride + j];
+    const int64_t tr = row_table ? (int64_t)row_table[b] : (int64_t)b;
+    const int table_ok = row_table == NULL || (tr >= 0 && tr < num_tables);
+    const int32_t g = table_ok ? page_table[tr * pt_stride + j] : -1;
     const int page_ok = (g >= 0 && (int64_t)g < num_pages);
 
     for (int i = 0; i < PG; ++i) {

@@ -247,6 +247,31 @@ def pin_shared_table_equals_copies(ora):
     assert np.array_equal(ora.paged_mqa_logits(base), ora.paged_mqa_logits(copy), equal_nan=True)
 
 
+def pin_request_map_equals_expanded_tables(ora):
+    """Rows mapped to request tables score exactly as rows given copies of
+    their request's table; an index outside the tables gives NaN at the
+    row's live positions."""
+    import dataclasses
+    base = W.varlen_workload(14, "fp8", tokens=[3, 1, 4], contexts=[150, 64, 260], table_width=5,
+                             num_pages=16, interleave=True)
+    tabs = base.page_table.reshape(3, 5)
+    copy = dataclasses.replace(base, page_table=tabs[base.row_table].reshape(-1).copy(), pt_stride=5,
+                               row_table=None, num_tables=0)
+    got = ora.paged_mqa_logits(base)
+    assert np.array_equal(got, ora.paged_mqa_logits(copy), equal_nan=True)
+    assert np.all(np.isfinite(got[~mask_of(base)]))
+    # only tables 0 and 1 declared (table 2 stays in the buffer): rows of
+    # request 2 and a negative index are outside
+    bad = dataclasses.replace(base, row_table=base.row_table.copy(), num_tables=2)
+    bad.row_table[0] = -1
+    out = ora.paged_mqa_logits(bad)
+    m = mask_of(bad)
+    for b in range(bad.rows):
+        want_nan = bad.row_table[b] < 0 or bad.row_table[b] >= 2
+        assert np.all(np.isnan(out[b][~m[b]]) == want_nan) and np.all(np.isneginf(out[b][m[b]]))
+    assert (bad.row_table == 2).sum() == 4 and bad.lengths()[0] > 0
+
+
 def pin_mask_edges(ora):
     """-inf exactly at p >= clamp(seqlen, 0, 64*width); finite below; padding never read."""
     seq = [0, 1, 63, 64, 65, 3 * P - 1, 3 * P, 3 * P + 5, -3, 2 ** 31 - 1, -2 ** 31]

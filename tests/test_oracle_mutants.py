@@ -23,9 +23,9 @@ MUTANTS = {
     "scale_after_relu": ("relu(s * dot)", "s * relu(dot)"),
     "no_relu": ("(x > 0.0 ? x : 0.0)", "(x)"),
     "relu_drops_nan": ("isnan(x) ? x : (x > 0.0 ? x : 0.0)", "(x > 0.0 ? x : 0.0)"),
-    "page_table_ignored": ("const int32_t g = page_table[(int64_t)b * pt_stride + j];",
-                           "const int32_t g = j;"),
-    "table_row_stride_ignored": ("page_table[(int64_t)b * pt_stride + j]", "page_table[j]"),
+    "page_table_ignored": ("const int32_t g = table_ok ? page_table[tr * pt_stride + j] : -1;",
+                           "const int32_t g = table_ok ? j : -1;"),
+    "table_row_stride_ignored": ("page_table[tr * pt_stride + j]", "page_table[j]"),
     "mask_off_by_one": ("if (p >= L) { o[i] = -INFINITY; continue; }",
                         "if (p > L) { o[i] = -INFINITY; continue; }"),
     "e4m3_bias_8": ("(int)e - 7", "(int)e - 8"),
@@ -48,6 +48,10 @@ MUTANTS = {
     "quant_last_dim_dropped": ("for (int d = 0; d < HD; ++d) {\n      const uint32_t u",
                                "for (int d = 0; d < HD - 1; ++d) {\n      const uint32_t u"),
     "quant_zero_scale": ("amax > 0.0f ? amax / 448.0f : 1.0f", "amax / 448.0f"),
+    "request_map_ignored": ("const int64_t tr = row_table ? (int64_t)row_table[b] : (int64_t)b;",
+                            "const int64_t tr = (int64_t)b;"),
+    "request_map_unchecked": ("const int table_ok = row_table == NULL || (tr >= 0 && tr < num_tables);",
+                              "const int table_ok = row_table == NULL || tr >= 0;"),
     "topk_ties_to_high_position": ("return (x->p > y->p) - (x->p < y->p);",
                                    "return (x->p < y->p) - (x->p > y->p);"),
     "topk_nan_first": ("if (xn != yn) return xn - yn;", "if (xn != yn) return yn - xn;"),

@@ -55,6 +55,8 @@ class Workload:
     page_table: np.ndarray   # int32, flat
     pt_stride: int
     seqlens: np.ndarray      # int32 [rows]
+    row_table: np.ndarray | None = None  # int32 [rows]: page-table row of each row (multi-request)
+    num_tables: int = 0
 
     @property
     def ncols(self) -> int:
@@ -244,6 +246,45 @@ def random_workload(seed: int, key_kind: str, rows: int, table_width: int, num_p
                     table_width=table_width, num_pages=num_pages, q=q, weights=w, kv=kv,
                     kv_stride=kv_stride, ks=ks, ks_offset=ks_off, ks_stride=ks_stride,
                     page_table=table.reshape(-1).copy(), pt_stride=stride, seqlens=seqlens)
+
+
+def varlen_workload(seed: int, key_kind: str, tokens, contexts, table_width: int, num_pages: int,
+                    interleave: bool = False, layout: str = "fused") -> Workload:
+    """Seeded prefill batch of several requests (tests and benchmark).
+
+    Request r contributes tokens[r] query rows and owns contexts[r] cached
+    positions; its token t (0-based) sees ceil(contexts[r] * (t+1) / tokens[r])
+    of them (causal growth, as in the single-request prefill).  Each request
+    has its own table (row r of page_table, stride table_width) of distinct
+    pool pages, -1 past its live pages; row_table maps each row to its
+    request.  Rows are grouped by request, or dealt round-robin over the
+    requests with ``interleave``.
+    Draws: q, weights, keys (as random_workload), then the tables.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    tokens = [int(t) for t in tokens]
+    contexts = [int(c) for c in contexts]
+    rows = sum(tokens)
+    q, w = draw_q_w(rng, rows)
+    kv, kv_stride, ks, ks_off, ks_stride = keys_from_normal(rng, num_pages, key_kind, layout)
+    R = len(tokens)
+    table = np.full((R, table_width), -1, dtype=np.int32)
+    for r in range(R):
+        nlive = min(table_width, (contexts[r] + PAGE - 1) // PAGE)
+        table[r, :nlive] = rng.permutation(num_pages)[:nlive]
+    req_rows = [(r, t) for r in range(R) for t in range(tokens[r])]
+    if interleave:
+        req_rows = []
+        for t in range(max(tokens) if tokens else 0):
+            req_rows += [(r, t) for r in range(R) if t < tokens[r]]
+    row_table = np.array([r for r, _ in req_rows], dtype=np.int32)
+    seqlens = np.array([(contexts[r] * (t + 1) + tokens[r] - 1) // tokens[r] for r, t in req_rows],
+                       dtype=np.int64).astype(np.int32)
+    return Workload(name=f"varlen seed={seed} requests={R}", key_kind=key_kind, rows=rows,
+                    table_width=table_width, num_pages=num_pages, q=q, weights=w, kv=kv,
+                    kv_stride=kv_stride, ks=ks, ks_offset=ks_off, ks_stride=ks_stride,
+                    page_table=table.reshape(-1).copy(), pt_stride=table_width, seqlens=seqlens,
+                    row_table=row_table, num_tables=R)
 
 
 # --------------------------------------------------------------------------
