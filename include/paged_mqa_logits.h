@@ -131,6 +131,42 @@ int idx_paged_mqa_logits_bf16(const void* q, const void* kv_pages, const float* 
                               int64_t page_table_row_stride, hipStream_t stream);
 
 /*
+ * Multi-request prefill: the query rows of several requests in one call, each
+ * request with its own page table and every row with its own causal length.
+ * The pages show a prefill of one request; a batch of several is the reading
+ * taken for serving ("The Dispatch Decision: Wiring a Triton Kernel into
+ * Production", section "The Problem That Led Here": the prefill path scores
+ * the query tokens of a request against its cached keys).
+ * Arguments as idx_paged_mqa_logits_fp8 except:
+ *   page_table   int32 tables, table t at page_table + t*page_table_row_stride
+ *                (table_width entries each).
+ *   row_table    int32 [rows], 4-byte aligned: the table (request) of each
+ *                row.  Rows of one request should be contiguous: a block of 4
+ *                consecutive rows reads each key page once per distinct table
+ *                among its rows.  A row whose index lies outside
+ *                [0, num_tables) scores NaN at its live positions.
+ *   num_tables   >= 0.
+ *   seqlens      per row: the positions that row sees (its causal limit).
+ * Every output element is written.
+ */
+int idx_paged_mqa_logits_varlen_fp8(const void* q, const void* kv_pages, const float* kscale,
+                                    const int32_t* page_table, const int32_t* row_table,
+                                    int32_t num_tables, const int32_t* seqlens, const float* weights,
+                                    float* out, int32_t rows, int32_t num_heads, int32_t head_dim,
+                                    int32_t table_width, int64_t num_pages, int64_t kv_page_stride,
+                                    int64_t kscale_page_stride, int64_t page_table_row_stride,
+                                    hipStream_t stream);
+
+/* bf16-key counterpart of idx_paged_mqa_logits_varlen_fp8 (kscale must be NULL). */
+int idx_paged_mqa_logits_varlen_bf16(const void* q, const void* kv_pages, const float* kscale,
+                                     const int32_t* page_table, const int32_t* row_table,
+                                     int32_t num_tables, const int32_t* seqlens, const float* weights,
+                                     float* out, int32_t rows, int32_t num_heads, int32_t head_dim,
+                                     int32_t table_width, int64_t num_pages, int64_t kv_page_stride,
+                                     int64_t kscale_page_stride, int64_t page_table_row_stride,
+                                     hipStream_t stream);
+
+/*
  * Top-k over logits rows: the selection the -inf-masked logits feed ("The
  * Final Gate: Validating a Custom Triton Indexer Kernel Before Production
  * Deployment", section "What the Test Output Reveals").  The pages give

@@ -35,6 +35,8 @@ IDX_ERR_LAUNCH = -5
 _SYMBOLS = (
     "idx_paged_mqa_logits_fp8",
     "idx_paged_mqa_logits_bf16",
+    "idx_paged_mqa_logits_varlen_fp8",
+    "idx_paged_mqa_logits_varlen_bf16",
     "idx_topk_logits",
     "idx_paged_mqa_topk_fp8",
     "idx_paged_mqa_topk_bf16",
@@ -67,6 +69,10 @@ def _load() -> ctypes.CDLL:
     for name in ("idx_paged_mqa_logits_fp8", "idx_paged_mqa_logits_bf16"):
         fn = getattr(lib, name)
         fn.argtypes = argtypes
+        fn.restype = ctypes.c_int
+    for name in ("idx_paged_mqa_logits_varlen_fp8", "idx_paged_mqa_logits_varlen_bf16"):
+        fn = getattr(lib, name)
+        fn.argtypes = argtypes[:4] + [ctypes.c_void_p, ctypes.c_int32] + argtypes[4:]
         fn.restype = ctypes.c_int
     lib.idx_topk_logits.argtypes = [
         ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
@@ -189,6 +195,57 @@ def idx_paged_mqa_logits_bf16(q, kv_pages, kscale, page_table, seqlens, weights,
                  check=check)
 
 
+def _call_varlen(name, q, kv_pages, kscale, page_table, row_table, seqlens, weights, out, *,
+                 num_tables, num_pages, table_width, page_table_row_stride, kv_page_stride,
+                 kscale_page_stride, rows, num_heads, head_dim, stream, check):
+    if isinstance(q, torch.Tensor):
+        rows = q.shape[0] if rows is None else rows
+    num_heads = NUM_HEADS if num_heads is None else num_heads
+    head_dim = HEAD_DIM if head_dim is None else head_dim
+    dev = q.device if isinstance(q, torch.Tensor) else None
+    status = getattr(_lib, name)(
+        _addr(q), _addr(kv_pages), _addr(kscale), _addr(page_table), _addr(row_table),
+        int(num_tables), _addr(seqlens), _addr(weights), _addr(out), int(rows), int(num_heads),
+        int(head_dim), int(table_width), int(num_pages), int(kv_page_stride),
+        int(kscale_page_stride), int(page_table_row_stride), _stream_handle(stream, dev))
+    if check and status != IDX_OK:
+        raise IdxError(status, f"{name}: {idx_status_string(status)}")
+    return status
+
+
+def idx_paged_mqa_logits_varlen_fp8(q, kv_pages, kscale, page_table, row_table, seqlens, weights,
+                                    out, *, num_tables, num_pages, table_width,
+                                    page_table_row_stride=None,
+                                    kv_page_stride=FP8_FUSED_PAGE_BYTES,
+                                    kscale_page_stride=FP8_FUSED_PAGE_BYTES, rows=None,
+                                    num_heads=None, head_dim=None, stream=None,
+                                    check=True) -> int:
+    """Several requests' query rows in one call: row b uses table row_table[b]
+    (at page_table + row_table[b]*page_table_row_stride) and its own seqlen."""
+    pts = table_width if page_table_row_stride is None else page_table_row_stride
+    return _call_varlen("idx_paged_mqa_logits_varlen_fp8", q, kv_pages, kscale, page_table,
+                        row_table, seqlens, weights, out, num_tables=num_tables,
+                        num_pages=num_pages, table_width=table_width, page_table_row_stride=pts,
+                        kv_page_stride=kv_page_stride, kscale_page_stride=kscale_page_stride,
+                        rows=rows, num_heads=num_heads, head_dim=head_dim, stream=stream,
+                        check=check)
+
+
+def idx_paged_mqa_logits_varlen_bf16(q, kv_pages, kscale, page_table, row_table, seqlens, weights,
+                                     out, *, num_tables, num_pages, table_width,
+                                     page_table_row_stride=None, kv_page_stride=BF16_PAGE_BYTES,
+                                     kscale_page_stride=0, rows=None, num_heads=None,
+                                     head_dim=None, stream=None, check=True) -> int:
+    """bf16-key counterpart of :func:`idx_paged_mqa_logits_varlen_fp8`."""
+    pts = table_width if page_table_row_stride is None else page_table_row_stride
+    return _call_varlen("idx_paged_mqa_logits_varlen_bf16", q, kv_pages, kscale, page_table,
+                        row_table, seqlens, weights, out, num_tables=num_tables,
+                        num_pages=num_pages, table_width=table_width, page_table_row_stride=pts,
+                        kv_page_stride=kv_page_stride, kscale_page_stride=kscale_page_stride,
+                        rows=rows, num_heads=num_heads, head_dim=head_dim, stream=stream,
+                        check=check)
+
+
 def idx_topk_logits(logits, seqlens, topk_idx, topk_val=None, *, k=None, rows=None, ncols=None,
                     row_stride=None, stream=None, check=True) -> int:
     """Per row b, the k largest of logits[b, :clamp(seqlens[b], 0, ncols)] (equal
@@ -291,7 +348,8 @@ def idx_store_keys_bf16(keys, slots, kv_pages, *, num_pages, n=None, kv_page_str
 
 
 __all__ = [
-    "idx_paged_mqa_logits_fp8", "idx_paged_mqa_logits_bf16", "idx_topk_logits",
+    "idx_paged_mqa_logits_fp8", "idx_paged_mqa_logits_bf16", "idx_paged_mqa_logits_varlen_fp8",
+    "idx_paged_mqa_logits_varlen_bf16", "idx_topk_logits",
     "idx_paged_mqa_topk_fp8", "idx_paged_mqa_topk_bf16", "idx_store_keys_fp8",
     "idx_store_keys_bf16", "idx_status_string",
     "idx_abi_version", "IdxError", "LIB_PATH", "NUM_HEADS", "HEAD_DIM", "PAGE_POSITIONS",

@@ -20,11 +20,14 @@
 //    of page slots of one row, keeps the row's query in registers across them
 //    and streams key bytes from HBM straight into the MFMA operand layout,
 //    prefetching the next page while the current one is multiplied.
-//  * shared   -- rows that share one page table (page_table_row_stride == 0:
-//    the query tokens of one prefill request).  A workgroup owns 4 rows x a
-//    chunk of pages; each page is loaded once into LDS (XOR-swizzled) and all
-//    4 waves multiply it against their own row's query, so key bytes are
-//    fetched once per 4 rows and the query stays in registers for the chunk.
+//  * shared   -- rows that share page tables: the query tokens of one
+//    prefill request (page_table_row_stride == 0), or of several requests
+//    with a row -> request table map.  A workgroup owns 4 rows x a chunk of
+//    pages; each page is loaded once into LDS (XOR-swizzled) and the waves
+//    whose rows use that table multiply it against their own row's query, so
+//    key bytes are fetched once per 4 rows and the query stays in registers
+//    for the chunk.  A block of 4 rows that straddles requests runs once per
+//    table.
 //
 // MFMA fragment layout (16x16x32 bf16, lane l, n = l % 16, g = l / 16):
 //   A (query)  row  h = 16*mb + n,  8 k-values,
@@ -66,6 +69,8 @@ struct Params {
   int64_t num_pages, kv_stride, ks_stride, pt_stride;
   int32_t rows, width;
   int32_t fill;       // 0: page slots past a row's live pages are left unwritten
+  const int32_t* rt;  // shared kernel: table index of each row (NULL: table 0 for all)
+  int32_t num_tables; // valid table indices [0, num_tables) when rt is set
 };
 
 // Raw key bytes of one page for one lane, already in B-fragment order:
@@ -707,8 +712,9 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(KEY 
 }
 
 // ---------------------------------------------------------------------------
-// shared kernel: rows share one page table.  Unit = (block of 4 rows, chunk of
-// `chunk` page slots); wave w scores row 4*rb + w.  Pages go through LDS.
+// shared kernel: rows share page tables (one, or one per request through a
+// row -> table map).  Unit = (block of 4 rows, chunk of `chunk` page slots);
+// wave w scores row 4*rb + w.  Pages go through LDS.
 constexpr int kSharedRows = 4;
 
 template <int KEY>
@@ -850,7 +856,6 @@ __global__ __launch_bounds__(64 * kSharedRows) void shared_kernel(Params p, int3
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int32_t ops = shared_dma_ops<KEY>(wave);  // DMA operations per page
   const int32_t width = p.width;
-  const int32_t* tab = p.pt;  // shared table (row stride 0)
 
   for (int64_t slot = blockIdx.x; slot < total_slots; slot += gridDim.x) {
     // Workgroup ids are dealt to the 8 XCDs round-robin; keep all chunks of a
@@ -867,73 +872,97 @@ __global__ __launch_bounds__(64 * kSharedRows) void shared_kernel(Params p, int3
     const int32_t j0 = c * chunk;
     const int32_t jend = min(j0 + chunk, width);
     const int32_t b = rb * kSharedRows + wave;
-    const bool row_ok = b < p.rows;
     float* orow = p.out + (int64_t)b * width * kPage;
 
-    // Longest live prefix over the block's rows decides which pages to load.
-    int32_t Lmax = 0;
+    // Table of each of the block's rows.  Rows of one request share a table;
+    // a block that straddles requests runs once per distinct table, with
+    // only that table's rows scoring (the other waves still copy their part
+    // of each page and meet every barrier).
+    int32_t tix[kSharedRows];
 #pragma unroll
     for (int r = 0; r < kSharedRows; ++r) {
       const int32_t br = rb * kSharedRows + r;
-      if (br < p.rows) Lmax = max(Lmax, clamp_len(load_uniform(p.sl, br), width));
+      tix[r] = br < p.rows ? (p.rt ? load_uniform(p.rt, br) : 0) : INT32_MIN;
     }
-    const int32_t L = row_ok ? clamp_len(load_uniform(p.sl, b), width) : 0;
-    const int32_t live_w = (L + kPage - 1) / kPage;
-    const int32_t jl = max(j0, min(jend, (Lmax + kPage - 1) / kPage));  // pages any row needs
-
-    if (j0 < jl) {
-      RowQuery rq;
-      if (row_ok && j0 < live_w) load_row_query(p, b, lane, rq);
-      // A page id outside the pool -- or a page past jl, issued only to keep
-      // the operation count per iteration constant -- is copied from the
-      // query buffer instead (always valid memory, at least 16 KiB).
-      uint32_t ok_bits = 0;  // bit t % NS: page j0 + t has a valid id
-      auto issue = [&](int32_t t) {
-        const int32_t j = j0 + t;
-        const int32_t g = j < jl ? load_uniform(tab, j) : -1;
-        const bool ok = page_ok(g, p.num_pages);
-        const int u = t % NS;
-        ok_bits = (uint32_t)uniform((int32_t)((ok_bits & ~(1u << u)) | ((ok ? 1u : 0u) << u)));
-        const uint8_t* page = ok ? p.kv + (int64_t)g * p.kv_stride : p.q;
-        const uint8_t* sc = (KEY == kFp8 && ok) ? p.ks + (int64_t)g * p.ks_stride : p.q + 8192;
-        shared_dma_page<KEY>(page, sc, slots + u * kSlot, wave, lane);
-      };
+    int32_t my_tix = tix[0];
 #pragma unroll
-      for (int t = 0; t < NS - 1; ++t) issue(t);
-      // The query was requested before these DMAs: wait for it here with them
-      // still in flight, so that no conservative wait lands in the page loop.
-      // (Wave 0 of the fp8 kernel has one more operation per page; waiting on
-      // the smaller count there costs it a part of page 0, no more.)
-      __builtin_amdgcn_s_waitcnt(wait_vm((NS - 1) * shared_dma_ops<KEY>(1)));
-      const int32_t st = row_ok ? 1 : 0;  // stores per iteration
-      for (int32_t t = 0; j0 + t < jl; ++t) {
-        const int32_t j = j0 + t;
-        const int u = t % NS;
-        // Operations issued after page t's DMA: the pages of the (NS-2) later
-        // DMAs and the stores of the min(t, NS-1) iterations since it.
-        const int32_t n_after = uniform(min(t, NS - 1) * st + (NS - 2) * ops);
-        // Every wave waits for its own part of page t; the barrier then makes
-        // the whole page visible -- and also guarantees that every wave is
-        // done with slot (t-1) % NS, which the next DMA overwrites.
-        wait_vm_n(n_after);
-        __builtin_amdgcn_s_barrier();
-        PageKeys<KEY> pk;
-        if (row_ok && j < live_w) read_shared_slot<KEY>(base + (uint32_t)(u * kSlot), lane, pk);
-        issue(t + NS - 1);
-        if (row_ok) {
-          if (j >= live_w) {
-            store_page(orow, j, 0, lane, 0.f);  // whole page past this row's length
-          } else if ((ok_bits >> u) & 1u) {
-            store_page(orow, j, L, lane, score_page<KEY>(rq, pk, lane));
-          } else {
-            store_bad_page(orow, j, L, lane);
+    for (int r = 1; r < kSharedRows; ++r) my_tix = (wave == r) ? tix[r] : my_tix;
+    for (int gi = 0; gi < kSharedRows; ++gi) {
+      const int32_t T = tix[gi];
+      bool lead = T != INT32_MIN;
+#pragma unroll
+      for (int r = 0; r < kSharedRows; ++r) lead = lead && !(r < gi && tix[r] == T);
+      if (!lead) continue;
+      // An index outside the tables reads no table: its rows score NaN.
+      const bool table_ok = p.rt == nullptr || (T >= 0 && T < p.num_tables);
+      const int32_t* tab = p.pt + (int64_t)(table_ok ? T : 0) * p.pt_stride;
+      const bool row_ok = b < p.rows && my_tix == T;
+
+      // Longest live prefix over the group's rows decides which pages to load.
+      int32_t Lmax = 0;
+#pragma unroll
+      for (int r = 0; r < kSharedRows; ++r) {
+        const int32_t br = rb * kSharedRows + r;
+        if (br < p.rows && tix[r] == T) Lmax = max(Lmax, clamp_len(load_uniform(p.sl, br), width));
+      }
+      const int32_t L = row_ok ? clamp_len(load_uniform(p.sl, b), width) : 0;
+      const int32_t live_w = (L + kPage - 1) / kPage;
+      const int32_t jl = max(j0, min(jend, (Lmax + kPage - 1) / kPage));  // pages any row needs
+
+      if (j0 < jl) {
+        RowQuery rq;
+        if (row_ok && j0 < live_w) load_row_query(p, b, lane, rq);
+        // A page id outside the pool -- or a page past jl, issued only to keep
+        // the operation count per iteration constant -- is copied from the
+        // query buffer instead (always valid memory, at least 16 KiB).
+        uint32_t ok_bits = 0;  // bit t % NS: page j0 + t has a valid id
+        auto issue = [&](int32_t t) {
+          const int32_t j = j0 + t;
+          const int32_t g = (j < jl && table_ok) ? load_uniform(tab, j) : -1;
+          const bool ok = page_ok(g, p.num_pages);
+          const int u = t % NS;
+          ok_bits = (uint32_t)uniform((int32_t)((ok_bits & ~(1u << u)) | ((ok ? 1u : 0u) << u)));
+          const uint8_t* page = ok ? p.kv + (int64_t)g * p.kv_stride : p.q;
+          const uint8_t* sc = (KEY == kFp8 && ok) ? p.ks + (int64_t)g * p.ks_stride : p.q + 8192;
+          shared_dma_page<KEY>(page, sc, slots + u * kSlot, wave, lane);
+        };
+#pragma unroll
+        for (int t = 0; t < NS - 1; ++t) issue(t);
+        // The query was requested before these DMAs: wait for it here with them
+        // still in flight, so that no conservative wait lands in the page loop.
+        // (Wave 0 of the fp8 kernel has one more operation per page; waiting on
+        // the smaller count there costs it a part of page 0, no more.)
+        __builtin_amdgcn_s_waitcnt(wait_vm((NS - 1) * shared_dma_ops<KEY>(1)));
+        const int32_t st = row_ok ? 1 : 0;  // stores per iteration
+        for (int32_t t = 0; j0 + t < jl; ++t) {
+          const int32_t j = j0 + t;
+          const int u = t % NS;
+          // Operations issued after page t's DMA: the pages of the (NS-2) later
+          // DMAs and the stores of the min(t, NS-1) iterations since it.
+          const int32_t n_after = uniform(min(t, NS - 1) * st + (NS - 2) * ops);
+          // Every wave waits for its own part of page t; the barrier then makes
+          // the whole page visible -- and also guarantees that every wave is
+          // done with slot (t-1) % NS, which the next DMA overwrites.
+          wait_vm_n(n_after);
+          __builtin_amdgcn_s_barrier();
+          PageKeys<KEY> pk;
+          if (row_ok && j < live_w) read_shared_slot<KEY>(base + (uint32_t)(u * kSlot), lane, pk);
+          issue(t + NS - 1);
+          if (row_ok) {
+            if (j >= live_w) {
+              store_page(orow, j, 0, lane, 0.f);  // whole page past this row's length
+            } else if ((ok_bits >> u) & 1u) {
+              store_page(orow, j, L, lane, score_page<KEY>(rq, pk, lane));
+            } else {
+              store_bad_page(orow, j, L, lane);
+            }
           }
         }
+        __builtin_amdgcn_s_waitcnt(wait_vm(0));
+        __builtin_amdgcn_s_barrier();  // LDS is reused by this workgroup's next unit
       }
-      __builtin_amdgcn_s_waitcnt(wait_vm(0));
-      __builtin_amdgcn_s_barrier();  // LDS is reused by this workgroup's next unit
-    }
-    if (row_ok && p.fill && jl < jend) fill_neg_inf(orow, jl, jend - jl, lane);
+      if (row_ok && p.fill && jl < jend) fill_neg_inf(orow, jl, jend - jl, lane);
+    }  // table groups
   }
 }
 
@@ -1397,7 +1426,8 @@ int launch(const void* q, const void* kv_pages, const float* kscale, const int32
            const int32_t* seqlens, const float* weights, float* out, int32_t rows,
            int32_t num_heads, int32_t head_dim, int32_t table_width, int64_t num_pages,
            int64_t kv_page_stride, int64_t kscale_page_stride, int64_t page_table_row_stride,
-           hipStream_t stream, bool fill = true) {
+           hipStream_t stream, bool fill = true, const int32_t* row_table = nullptr,
+           int32_t num_tables = 1) {
   const int st = validate(KEY, q, kv_pages, kscale, page_table, seqlens, weights, out, rows,
                           num_heads, head_dim, table_width, num_pages, kv_page_stride,
                           kscale_page_stride, page_table_row_stride);
@@ -1418,9 +1448,11 @@ int launch(const void* q, const void* kv_pages, const float* kscale, const int32
   p.rows = rows;
   p.width = table_width;
   p.fill = fill ? 1 : 0;
+  p.rt = row_table;
+  p.num_tables = num_tables;
 
   (void)hipGetLastError();  // start from a clean error state
-  if (page_table_row_stride != 0 || rows == 1) {
+  if (row_table == nullptr && (page_table_row_stride != 0 || rows == 1)) {
     if (rows <= kBalancedMaxRows) {
       const int64_t slots = (int64_t)rows * table_width;
       const int64_t want = (slots + 7) / 8;
@@ -1431,7 +1463,7 @@ int launch(const void* q, const void* kv_pages, const float* kscale, const int32
       return hipGetLastError() == hipSuccess ? IDX_OK : IDX_ERR_LAUNCH;
     }
   }
-  if (page_table_row_stride == 0 && rows > 1) {
+  if (row_table != nullptr || (page_table_row_stride == 0 && rows > 1)) {
     const int32_t row_blocks = (rows + kSharedRows - 1) / kSharedRows;
     // Whole rows per unit (the query is read once) unless that leaves too few
     // units to fill the chip; then split the table into chunks.
@@ -1515,6 +1547,25 @@ int launch_logits_topk(const void* q, const void* kv_pages, const float* kscale,
 }
 
 template <int KEY>
+int launch_varlen(const void* q, const void* kv_pages, const float* kscale, const int32_t* page_table,
+                  const int32_t* row_table, int32_t num_tables, const int32_t* seqlens,
+                  const float* weights, float* out, int32_t rows, int32_t num_heads, int32_t head_dim,
+                  int32_t table_width, int64_t num_pages, int64_t kv_page_stride,
+                  int64_t kscale_page_stride, int64_t page_table_row_stride, hipStream_t stream) {
+  const int st = validate(KEY, q, kv_pages, kscale, page_table, seqlens, weights, out, rows, num_heads,
+                          head_dim, table_width, num_pages, kv_page_stride, kscale_page_stride,
+                          page_table_row_stride);
+  if (st != IDX_OK) return st;
+  if (num_tables < 0) return IDX_ERR_SHAPE;
+  if (rows == 0 || table_width == 0) return IDX_OK;
+  if (!row_table) return IDX_ERR_NULL;
+  if (!aligned(row_table, 4)) return IDX_ERR_ALIGN;
+  return launch<KEY>(q, kv_pages, kscale, page_table, seqlens, weights, out, rows, num_heads, head_dim,
+                     table_width, num_pages, kv_page_stride, kscale_page_stride, page_table_row_stride,
+                     stream, /*fill=*/true, row_table, num_tables);
+}
+
+template <int KEY>
 int store_keys(const void* keys, const int64_t* slots, int64_t n, void* kv_pages, float* kscale,
                int64_t num_pages, int64_t kv_page_stride, int64_t kscale_page_stride,
                hipStream_t stream) {
@@ -1564,6 +1615,30 @@ int idx_paged_mqa_logits_bf16(const void* q, const void* kv_pages, const float* 
   return launch<kBf16>(q, kv_pages, kscale, page_table, seqlens, weights, out, rows, num_heads,
                        head_dim, table_width, num_pages, kv_page_stride, kscale_page_stride,
                        page_table_row_stride, stream);
+}
+
+int idx_paged_mqa_logits_varlen_fp8(const void* q, const void* kv_pages, const float* kscale,
+                                    const int32_t* page_table, const int32_t* row_table,
+                                    int32_t num_tables, const int32_t* seqlens, const float* weights,
+                                    float* out, int32_t rows, int32_t num_heads, int32_t head_dim,
+                                    int32_t table_width, int64_t num_pages, int64_t kv_page_stride,
+                                    int64_t kscale_page_stride, int64_t page_table_row_stride,
+                                    hipStream_t stream) {
+  return launch_varlen<kFp8>(q, kv_pages, kscale, page_table, row_table, num_tables, seqlens, weights, out,
+                             rows, num_heads, head_dim, table_width, num_pages, kv_page_stride,
+                             kscale_page_stride, page_table_row_stride, stream);
+}
+
+int idx_paged_mqa_logits_varlen_bf16(const void* q, const void* kv_pages, const float* kscale,
+                                     const int32_t* page_table, const int32_t* row_table,
+                                     int32_t num_tables, const int32_t* seqlens, const float* weights,
+                                     float* out, int32_t rows, int32_t num_heads, int32_t head_dim,
+                                     int32_t table_width, int64_t num_pages, int64_t kv_page_stride,
+                                     int64_t kscale_page_stride, int64_t page_table_row_stride,
+                                     hipStream_t stream) {
+  return launch_varlen<kBf16>(q, kv_pages, kscale, page_table, row_table, num_tables, seqlens, weights,
+                              out, rows, num_heads, head_dim, table_width, num_pages, kv_page_stride,
+                              kscale_page_stride, page_table_row_stride, stream);
 }
 
 int idx_topk_logits(const float* logits, int64_t row_stride, const int32_t* seqlens, int32_t rows,

@@ -43,6 +43,9 @@ def lib():
                                   ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                   ctypes.c_void_p]
     l.idx_topk_logits.restype = ctypes.c_int
+    for name in ("idx_paged_mqa_logits_varlen_fp8", "idx_paged_mqa_logits_varlen_bf16"):
+        getattr(l, name).argtypes = args[:4] + [ctypes.c_void_p, ctypes.c_int32] + args[4:]
+        getattr(l, name).restype = ctypes.c_int
     for name in ("idx_paged_mqa_topk_fp8", "idx_paged_mqa_topk_bf16"):
         getattr(l, name).argtypes = args[:-1] + [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                                  ctypes.c_void_p]
@@ -55,6 +58,7 @@ def lib():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "idx_abi_version", "idx_paged_mqa_logits_bf16", "idx_paged_mqa_logits_fp8",
+        "idx_paged_mqa_logits_varlen_bf16", "idx_paged_mqa_logits_varlen_fp8",
         "idx_paged_mqa_topk_bf16", "idx_paged_mqa_topk_fp8", "idx_status_string",
         "idx_store_keys_bf16", "idx_store_keys_fp8", "idx_topk_logits"])
 
@@ -219,3 +223,32 @@ TF, TB = "idx_paged_mqa_topk_fp8", "idx_paged_mqa_topk_bf16"
 ])
 def test_fused_topk_host_validation(lib, name, kw, status):
     assert _fused(lib, name, **kw) == status
+
+
+def _varlen(lib, name, rt=4, ntab=2, **kw):
+    a = dict(q=16, kv=16, ks=16, pt=4, sl=4, w=16, out=16, rows=1, heads=64, dim=128, width=1,
+             num_pages=1, kv_stride=8448, ks_stride=8448, pt_stride=1)
+    if name.endswith("bf16"):
+        a.update(ks=None, kv_stride=16384, ks_stride=0)
+    a.update(kw)
+    return getattr(lib, name)(a["q"], a["kv"], a["ks"], a["pt"], rt, ntab, a["sl"], a["w"], a["out"],
+                              a["rows"], a["heads"], a["dim"], a["width"], a["num_pages"],
+                              a["kv_stride"], a["ks_stride"], a["pt_stride"], None)
+
+
+VF, VB = "idx_paged_mqa_logits_varlen_fp8", "idx_paged_mqa_logits_varlen_bf16"
+
+
+@pytest.mark.parametrize("name,kw,status", [
+    (VF, dict(heads=32), IDX_ERR_UNSUPPORTED),
+    (VF, dict(ntab=-1), IDX_ERR_SHAPE),
+    (VB, dict(kv_stride=8448), IDX_ERR_SHAPE),
+    (VF, dict(rows=0, rt=None, q=None), IDX_OK),              # nothing to do
+    (VF, dict(rt=None), IDX_ERR_NULL),
+    (VF, dict(q=None), IDX_ERR_NULL),
+    (VB, dict(ks=16), IDX_ERR_NULL),
+    (VF, dict(rt=2), IDX_ERR_ALIGN),
+    (VF, dict(out=4), IDX_ERR_ALIGN),
+])
+def test_varlen_host_validation(lib, name, kw, status):
+    assert _varlen(lib, name, **kw) == status

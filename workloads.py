@@ -287,6 +287,19 @@ def varlen_workload(seed: int, key_kind: str, tokens, contexts, table_width: int
                     row_table=row_table, num_tables=R)
 
 
+VARLEN_NAME = "bf16 multi-request prefill, 4 requests, 4096 rows, width=128"
+
+
+def varlen_config() -> Workload:
+    """Multi-request prefill at the single-request prefill's scale: 4096 query
+    rows from four requests (1024, 512, 2048 and 512 tokens) over contexts of
+    5632, 2048, 8192 and 1024 positions, bf16 keys, tables of 128 pages."""
+    wl = varlen_workload(1005, "bf16", tokens=[1024, 512, 2048, 512],
+                         contexts=[5632, 2048, 8192, 1024], table_width=128, num_pages=512)
+    wl.name = VARLEN_NAME
+    return wl
+
+
 # --------------------------------------------------------------------------
 # device placement (plumbing for the library side)
 
@@ -301,6 +314,7 @@ class DeviceWorkload:
     page_table: torch.Tensor
     seqlens: torch.Tensor
     out: torch.Tensor
+    row_table: torch.Tensor | None = None
 
 
 def to_device(wl: Workload, device="cuda", out_fill: float = float("nan")) -> DeviceWorkload:
@@ -319,12 +333,23 @@ def to_device(wl: Workload, device="cuda", out_fill: float = float("nan")) -> De
     pt = torch.from_numpy(wl.page_table).to(dev)
     sl = torch.from_numpy(wl.seqlens).to(dev)
     out = torch.full((wl.rows, wl.ncols), out_fill, dtype=torch.float32, device=dev)
-    return DeviceWorkload(wl, q, w, kv, ks, kscale_addr, pt, sl, out)
+    rt = None if wl.row_table is None else torch.from_numpy(wl.row_table).to(dev)
+    return DeviceWorkload(wl, q, w, kv, ks, kscale_addr, pt, sl, out, rt)
 
 
 def run_library(dw: DeviceWorkload, lib_module, stream=None, check: bool = True) -> int:
-    """Call the library entry point matching the workload's key kind."""
+    """Call the library entry point matching the workload's key kind (the
+    multi-request entry points when rows map to request tables)."""
     wl = dw.wl
+    if wl.row_table is not None:
+        fn = (lib_module.idx_paged_mqa_logits_varlen_fp8 if wl.key_kind == "fp8"
+              else lib_module.idx_paged_mqa_logits_varlen_bf16)
+        return fn(dw.q, dw.kv, dw.kscale_addr if wl.key_kind == "fp8" else None, dw.page_table,
+                  dw.row_table, dw.seqlens, dw.weights, dw.out, num_tables=wl.num_tables,
+                  num_pages=wl.num_pages, table_width=wl.table_width,
+                  page_table_row_stride=wl.pt_stride, kv_page_stride=wl.kv_stride,
+                  kscale_page_stride=wl.ks_stride if wl.key_kind == "fp8" else 0,
+                  rows=wl.rows, stream=stream, check=check)
     if wl.key_kind == "fp8":
         return lib_module.idx_paged_mqa_logits_fp8(
             dw.q, dw.kv, dw.kscale_addr, dw.page_table, dw.seqlens, dw.weights, dw.out,
