@@ -13,7 +13,8 @@ Prints ONE JSON line:
   cpu_baseline   the CPU oracle timed on a bounded row sample of the same workload
   secondary      same measurements for the 128-page decode, the 513-slot control
                  of the default workload, the bf16 prefill (MFMA roofline), the
-                 crossed variants (bf16-key decode, fp8-key prefill), the fused
+                 crossed variants (bf16-key decode, fp8-key prefill), a
+                 multi-request prefill (four requests, 4096 rows), the fused
                  logits + top-2048 call (with the top-k kernel alone) on the
                  default workload and the prefill, and the fp8 key store
 
@@ -61,15 +62,19 @@ def algorithmic_work(wl):
     per live page.  Writes: the whole fixed-shape output (4 B per slot).
     FLOPs: 2 * 64 * 128 per live (row, position) pair.
     """
+    import numpy as np
+
     import workloads as W
     live = wl.live_positions()
     per_pos = (W.HEAD_DIM + 4) if wl.key_kind == "fp8" else 2 * W.HEAD_DIM
     reads = live * per_pos + wl.rows * (W.NUM_HEADS * W.HEAD_DIM * 2 + W.NUM_HEADS * 4 + 4) \
         + 4 * wl.live_pages()
-    if wl.pt_stride == 0:  # one shared table and one key set for every row
-        L = int(wl.lengths().max())
-        reads = L * per_pos + wl.rows * (W.NUM_HEADS * W.HEAD_DIM * 2 + W.NUM_HEADS * 4 + 4) \
-            + 4 * ((L + W.PAGE - 1) // W.PAGE)
+    if wl.pt_stride == 0 or wl.row_table is not None:  # key sets shared by the rows of a request
+        lens = wl.lengths()
+        req = np.zeros(wl.rows, dtype=np.int64) if wl.row_table is None else wl.row_table
+        Ls = [int(lens[req == r].max()) for r in np.unique(req)]
+        reads = sum(L * per_pos + 4 * ((L + W.PAGE - 1) // W.PAGE) for L in Ls) \
+            + wl.rows * (W.NUM_HEADS * W.HEAD_DIM * 2 + W.NUM_HEADS * 4 + 4)
     writes = wl.rows * wl.ncols * 4
     flops = 2 * W.NUM_HEADS * W.HEAD_DIM * live
     return reads, writes, flops
@@ -87,7 +92,7 @@ def measure(cfg, steps: int, warmup: int, topk: int | None = None):
     import workloads as W
 
     t0 = time.perf_counter()
-    wl = W.config(cfg)
+    wl = W.varlen_config() if cfg == "varlen" else W.config(cfg)
     log(f"config {cfg}: generated in {time.perf_counter() - t0:.1f}s "
         f"({wl.live_positions()} live positions)")
     base = W.to_device(wl)
@@ -290,7 +295,7 @@ def main() -> int:
 
     secondary = {}
     if not args.no_secondary:
-        for c in (2, "3c", 4, "2b", "4f"):
+        for c in (2, "3c", 4, "2b", "4f", "varlen"):
             if str(c) == str(cfg):
                 continue
             _, r = measure(c, max(10, args.steps // 2), max(3, args.warmup // 2))
@@ -299,7 +304,7 @@ def main() -> int:
                 "workload": r["name"], "kernel_ms_mean": round(r["kernel_ms_mean"], 5),
                 "positions_per_s": r["positions_per_s_kernel"],
             }
-            if r["shared_table"]:  # prefill: one key read serves many rows
+            if r["shared_table"] or c == "varlen":  # prefill: one key read serves many rows
                 entry.update(bound="mfma", achieved_tflops=round(r["tflops"], 2),
                              peak_tflops=BF16_MFMA_PEAK_TFLOPS,
                              frac=round(r["tflops"] / BF16_MFMA_PEAK_TFLOPS, 4),

@@ -841,8 +841,8 @@ __device__ __forceinline__ void read_shared_slot(uint32_t sb, int lane, PageKeys
 // waves multiply it against their own row's query; one barrier per page.
 constexpr int kSharedSlots = 2;
 
-template <int KEY>
-__global__ __launch_bounds__(64 * kSharedRows) void shared_kernel(Params p, int32_t row_blocks,
+template <int KEY, bool MULTI>
+__global__ __launch_bounds__(64 * kSharedRows) __attribute__((amdgpu_waves_per_eu(MULTI ? 2 : 1))) void shared_kernel(Params p, int32_t row_blocks,
                                                                   int32_t chunk, int32_t chunks,
                                                                   int32_t rb_per_xcd,
                                                                   int64_t total_slots) {
@@ -857,7 +857,12 @@ __global__ __launch_bounds__(64 * kSharedRows) void shared_kernel(Params p, int3
   const int32_t ops = shared_dma_ops<KEY>(wave);  // DMA operations per page
   const int32_t width = p.width;
 
-  for (int64_t slot = blockIdx.x; slot < total_slots; slot += gridDim.x) {
+  // MULTI: four groups per (row block, chunk) unit, the group index slowest
+  // (total_slots is a multiple of 8, so a unit keeps its XCD in every group).
+  const int64_t units = MULTI ? 4 * total_slots : total_slots;
+  for (int64_t us = blockIdx.x; us < units; us += gridDim.x) {
+    const int gi = MULTI ? (int)(us / total_slots) : 0;
+    const int64_t slot = MULTI ? us % total_slots : us;
     // Workgroup ids are dealt to the 8 XCDs round-robin; keep all chunks of a
     // row block on one XCD (its query rows stay in that L2) and hand out row
     // blocks longest-first (largest index first).
@@ -875,35 +880,31 @@ __global__ __launch_bounds__(64 * kSharedRows) void shared_kernel(Params p, int3
     float* orow = p.out + (int64_t)b * width * kPage;
 
     // Table of each of the block's rows.  Rows of one request share a table;
-    // a block that straddles requests runs once per distinct table, with
-    // only that table's rows scoring (the other waves still copy their part
-    // of each page and meet every barrier).
-    int32_t tix[kSharedRows];
-#pragma unroll
-    for (int r = 0; r < kSharedRows; ++r) {
-      const int32_t br = rb * kSharedRows + r;
-      tix[r] = br < p.rows ? (p.rt ? load_uniform(p.rt, br) : 0) : INT32_MIN;
-    }
-    int32_t my_tix = tix[0];
-#pragma unroll
-    for (int r = 1; r < kSharedRows; ++r) my_tix = (wave == r) ? tix[r] : my_tix;
-    for (int gi = 0; gi < kSharedRows; ++gi) {
-      const int32_t T = tix[gi];
-      bool lead = T != INT32_MIN;
-#pragma unroll
-      for (int r = 0; r < kSharedRows; ++r) lead = lead && !(r < gi && tix[r] == T);
+    // a block that straddles requests is scored once per distinct table (the
+    // unit's group gi: the table of the block's row gi, if no earlier row of
+    // the block has it), with only that table's rows scoring -- the other
+    // waves still copy their part of each page and meet every barrier.
+    // Table indices are scalar loads, re-read where needed.
+    auto table_of = [&](int32_t br) -> int32_t { return load_uniform(p.rt, br); };
+    const int32_t T = MULTI ? table_of(rb * kSharedRows + gi) : 0;
+    if constexpr (MULTI) {
+      if (rb * kSharedRows + gi >= p.rows) continue;
+      bool lead = true;
+      for (int r = 0; r < gi; ++r) lead = lead && table_of(rb * kSharedRows + r) != T;
       if (!lead) continue;
+    }
+    {
       // An index outside the tables reads no table: its rows score NaN.
-      const bool table_ok = p.rt == nullptr || (T >= 0 && T < p.num_tables);
-      const int32_t* tab = p.pt + (int64_t)(table_ok ? T : 0) * p.pt_stride;
-      const bool row_ok = b < p.rows && my_tix == T;
+      const bool table_ok = !MULTI || (T >= 0 && T < p.num_tables);
+      const int32_t* tab = MULTI ? p.pt + (int64_t)(table_ok ? T : 0) * p.pt_stride : p.pt;
+      const bool row_ok = b < p.rows && (!MULTI || table_of(b) == T);
 
       // Longest live prefix over the group's rows decides which pages to load.
       int32_t Lmax = 0;
 #pragma unroll
       for (int r = 0; r < kSharedRows; ++r) {
         const int32_t br = rb * kSharedRows + r;
-        if (br < p.rows && tix[r] == T) Lmax = max(Lmax, clamp_len(load_uniform(p.sl, br), width));
+        if (br < p.rows && (!MULTI || table_of(br) == T)) Lmax = max(Lmax, clamp_len(load_uniform(p.sl, br), width));
       }
       const int32_t L = row_ok ? clamp_len(load_uniform(p.sl, b), width) : 0;
       const int32_t live_w = (L + kPage - 1) / kPage;
@@ -962,7 +963,7 @@ __global__ __launch_bounds__(64 * kSharedRows) void shared_kernel(Params p, int3
         __builtin_amdgcn_s_barrier();  // LDS is reused by this workgroup's next unit
       }
       if (row_ok && p.fill && jl < jend) fill_neg_inf(orow, jl, jend - jl, lane);
-    }  // table groups
+    }
   }
 }
 
@@ -1474,9 +1475,14 @@ int launch(const void* q, const void* kv_pages, const float* kscale, const int32
     chunks = (table_width + chunk - 1) / chunk;
     const int32_t rb_per_xcd = (row_blocks + 7) / 8;
     const int64_t total = (int64_t)8 * rb_per_xcd * chunks;
-    const int64_t grid = total < kMaxGrid ? total : kMaxGrid;
-    shared_kernel<KEY><<<dim3((uint32_t)grid), dim3(64 * kSharedRows), 0, stream>>>(
-        p, row_blocks, chunk, chunks, rb_per_xcd, total);
+    const int64_t units = (row_table != nullptr) ? 4 * total : total;
+    const int64_t grid = units < kMaxGrid ? units : kMaxGrid;
+    if (row_table != nullptr)
+      shared_kernel<KEY, true><<<dim3((uint32_t)grid), dim3(64 * kSharedRows), 0, stream>>>(
+          p, row_blocks, chunk, chunks, rb_per_xcd, total);
+    else
+      shared_kernel<KEY, false><<<dim3((uint32_t)grid), dim3(64 * kSharedRows), 0, stream>>>(
+          p, row_blocks, chunk, chunks, rb_per_xcd, total);
   } else {
     constexpr int per_unit = kRowwisePPW * kRowwiseWaves;
     const int32_t units_per_row = (table_width + per_unit - 1) / per_unit;
