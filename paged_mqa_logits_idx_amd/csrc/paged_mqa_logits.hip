@@ -559,6 +559,103 @@ __device__ __forceinline__ void fill_rest(const Params& p, FillCursor& fc, int l
   } while (fill_next_segment(p, fc));
 }
 
+// bf16 page from its LDS slot into the lane's B fragments (rows of 256 B,
+// 16-byte chunk c of row i at chunk c ^ (i % 16)): lane (g, n) reads chunks
+// 4g .. 4g+3 of rows n, 16+n, 32+n, 48+n.  Waits
+// until at most N vector-memory operations are outstanding first (the
+// compiler does not see these reads, so it adds no wait for the DMAs still in
+// flight into other slots).
+template <int N>
+__device__ __forceinline__ void read_slot_bf16(uint32_t sb, int lane, PageKeys<kBf16>& pk) {
+  const int n = lane & 15, g = lane >> 4;
+  uint32_t a[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) a[v] = sb + (uint32_t)(n * 256 + 16 * ((4 * g + v) ^ n));
+  asm volatile(
+      "s_waitcnt vmcnt(%20)\n\t"
+      "ds_read_b128 %0, %16\n\t"
+      "ds_read_b128 %1, %17\n\t"
+      "ds_read_b128 %2, %18\n\t"
+      "ds_read_b128 %3, %19\n\t"
+      "ds_read_b128 %4, %16 offset:4096\n\t"
+      "ds_read_b128 %5, %17 offset:4096\n\t"
+      "ds_read_b128 %6, %18 offset:4096\n\t"
+      "ds_read_b128 %7, %19 offset:4096\n\t"
+      "ds_read_b128 %8, %16 offset:8192\n\t"
+      "ds_read_b128 %9, %17 offset:8192\n\t"
+      "ds_read_b128 %10, %18 offset:8192\n\t"
+      "ds_read_b128 %11, %19 offset:8192\n\t"
+      "ds_read_b128 %12, %16 offset:12288\n\t"
+      "ds_read_b128 %13, %17 offset:12288\n\t"
+      "ds_read_b128 %14, %18 offset:12288\n\t"
+      "ds_read_b128 %15, %19 offset:12288\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(pk.v[0][0]), "=&v"(pk.v[0][1]), "=&v"(pk.v[0][2]), "=&v"(pk.v[0][3]),
+        "=&v"(pk.v[1][0]), "=&v"(pk.v[1][1]), "=&v"(pk.v[1][2]), "=&v"(pk.v[1][3]),
+        "=&v"(pk.v[2][0]), "=&v"(pk.v[2][1]), "=&v"(pk.v[2][2]), "=&v"(pk.v[2][3]),
+        "=&v"(pk.v[3][0]), "=&v"(pk.v[3][1]), "=&v"(pk.v[3][2]), "=&v"(pk.v[3][3])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "n"(N)
+      : "memory");
+  pk.s = 1.0f;
+}
+
+// One bf16 page into a wave's 16 KiB slot by DMA: 16 operations of 1 KiB
+// (4 rows of 256 B each), the chunk swizzle applied on the source side since
+// the DMA destination is lane-linear.
+constexpr int kBf16SlotBytes = 16384;
+constexpr int kBf16DmaOps = 16;
+__device__ __forceinline__ void dma_page_bf16(const uint8_t* keys, lds_u8* slot, int lane) {
+  const int r = lane >> 4, c = lane & 15;
+#pragma unroll
+  for (int t = 0; t < kBf16DmaOps; ++t) {
+    const int i = 4 * t + r;
+    __builtin_amdgcn_global_load_lds((global_ptr)(keys + i * 256 + 16 * (c ^ (i & 15))),
+                                     (lds_ptr)(slot + 1024 * t), 16, 0, 0);
+  }
+}
+
+// Live bf16 pages [ja, jb) of row b through the wave's one LDS slot: page t+1
+// is requested as soon as page t is in registers, and flies while page t is
+// multiplied.
+__device__ __forceinline__ void row_pages_dma_bf16(const Params& p, int32_t b, int32_t ja, int32_t jb,
+                                                   int32_t L, int lane, lds_u8* slot) {
+  RowQuery rq;
+  load_row_query(p, b, lane, rq);
+  const int32_t* tab = p.pt + (int64_t)b * p.pt_stride;
+  float* orow = p.out + (int64_t)b * p.width * kPage;
+  // A page id outside the pool is never dereferenced: its DMA reads the row's
+  // own query (16 KiB, always valid memory) and its logits become NaN.
+  const uint8_t* safe = p.q + (int64_t)b * (kHeads * kDim * 2);
+  const int32_t J = jb - ja;
+  const int32_t g0 = load_uniform(tab, ja);
+  bool ok = page_ok(g0, p.num_pages);
+  dma_page_bf16(ok ? p.kv + (int64_t)g0 * p.kv_stride : safe, slot, lane);
+  // The query was requested before the DMA: wait for it here with the DMA in
+  // flight, so that no conservative wait lands in the page loop.
+  __builtin_amdgcn_s_waitcnt(wait_vm(kBf16DmaOps));
+  const uint32_t sb = (uint32_t)(uintptr_t)slot;
+  int32_t g_ahead = (1 < J) ? load_uniform(tab, ja + 1) : -1;
+  for (int32_t tt = 0; tt < J; ++tt) {
+    // Operations issued after page tt's DMA: the store of iteration tt-1.
+    PageKeys<kBf16> pk;
+    if (tt == 0)
+      read_slot_bf16<0>(sb, lane, pk);
+    else
+      read_slot_bf16<1>(sb, lane, pk);
+    const bool cur_ok = ok;
+    const int32_t g = g_ahead;
+    g_ahead = (tt + 2 < J) ? load_uniform(tab, ja + tt + 2) : -1;
+    if (tt + 1 < J) {
+      ok = page_ok(g, p.num_pages);
+      dma_page_bf16(ok ? p.kv + (int64_t)g * p.kv_stride : safe, slot, lane);
+    }
+    if (cur_ok)
+      store_page(orow, ja + tt, L, lane, score_page<kBf16>(rq, pk, lane));
+    else
+      store_bad_page(orow, ja + tt, L, lane);
+  }
+}
+
 // Live pages [ja, jb) of row b through the wave's NS LDS slots: NS pages are
 // in flight while one is multiplied.
 template <int NS>
@@ -662,7 +759,7 @@ __device__ __forceinline__ void live_share(const Params& p, int64_t s, int64_t e
       if constexpr (KEY == kFp8)
         row_pages_dma<NS>(p, r, ja, jb, L, lane, my_slots);
       else
-        row_pages<KEY, 2>(p, r, ja, jb, L, lane);
+        row_pages_dma_bf16(p, r, ja, jb, L, lane, my_slots);
     }
     pos = uniform(excl + jb);
     excl = uniform(excl + lp);
@@ -671,13 +768,14 @@ __device__ __forceinline__ void live_share(const Params& p, int64_t s, int64_t e
 }
 
 template <int KEY, int WAVES, int NS>
-__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(KEY == kFp8 ? 2 : 1, 2))) void balanced_kernel(Params p) {
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2))) void balanced_kernel(Params p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nw = (int64_t)gridDim.x * WAVES;
   const int64_t wid = (int64_t)blockIdx.x * WAVES + wave;
   const int32_t rows = p.rows, width = p.width;
-  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[(KEY == kFp8) ? WAVES * NS * kSlotBytes : 16];
+  constexpr int kWaveLds = (KEY == kFp8) ? NS * kSlotBytes : kBf16SlotBytes;  // per wave
+  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[WAVES * kWaveLds];
   lds_u8* dma_slots = (lds_u8*)lds_raw;
 
   // (1) total live pages, then this wave's range [s, e) of them.
@@ -703,11 +801,11 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(KEY 
   FillCursor fc = fill_cursor(p, wid, nw);
   if (!p.fill) fc.z = fc.a;  // nothing to write past the live pages
   if (2 * blockIdx.x >= gridDim.x) {
-    if (s < e) live_share<KEY, NS>(p, s, e, lane, dma_slots + wave * NS * kSlotBytes);
+    if (s < e) live_share<KEY, NS>(p, s, e, lane, dma_slots + wave * kWaveLds);
     fill_rest(p, fc, lane);
   } else {
     fill_rest(p, fc, lane);
-    if (s < e) live_share<KEY, NS>(p, s, e, lane, dma_slots + wave * NS * kSlotBytes);
+    if (s < e) live_share<KEY, NS>(p, s, e, lane, dma_slots + wave * kWaveLds);
   }
 }
 
@@ -765,44 +863,6 @@ __device__ __forceinline__ void shared_dma_page(const uint8_t* page, const uint8
   }
 }
 
-// bf16 page from its LDS slot into the lane's B fragments (layout of LdsPage):
-// lane (g, n) reads chunks 4g .. 4g+3 of rows n, 16+n, 32+n, 48+n.  Waits
-// until at most N vector-memory operations are outstanding first (the
-// compiler does not see these reads, so it adds no wait for the DMAs still in
-// flight into other slots).
-template <int N>
-__device__ __forceinline__ void read_slot_bf16(uint32_t sb, int lane, PageKeys<kBf16>& pk) {
-  const int n = lane & 15, g = lane >> 4;
-  uint32_t a[4];
-#pragma unroll
-  for (int v = 0; v < 4; ++v) a[v] = sb + (uint32_t)(n * 256 + 16 * ((4 * g + v) ^ n));
-  asm volatile(
-      "s_waitcnt vmcnt(%20)\n\t"
-      "ds_read_b128 %0, %16\n\t"
-      "ds_read_b128 %1, %17\n\t"
-      "ds_read_b128 %2, %18\n\t"
-      "ds_read_b128 %3, %19\n\t"
-      "ds_read_b128 %4, %16 offset:4096\n\t"
-      "ds_read_b128 %5, %17 offset:4096\n\t"
-      "ds_read_b128 %6, %18 offset:4096\n\t"
-      "ds_read_b128 %7, %19 offset:4096\n\t"
-      "ds_read_b128 %8, %16 offset:8192\n\t"
-      "ds_read_b128 %9, %17 offset:8192\n\t"
-      "ds_read_b128 %10, %18 offset:8192\n\t"
-      "ds_read_b128 %11, %19 offset:8192\n\t"
-      "ds_read_b128 %12, %16 offset:12288\n\t"
-      "ds_read_b128 %13, %17 offset:12288\n\t"
-      "ds_read_b128 %14, %18 offset:12288\n\t"
-      "ds_read_b128 %15, %19 offset:12288\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(pk.v[0][0]), "=&v"(pk.v[0][1]), "=&v"(pk.v[0][2]), "=&v"(pk.v[0][3]),
-        "=&v"(pk.v[1][0]), "=&v"(pk.v[1][1]), "=&v"(pk.v[1][2]), "=&v"(pk.v[1][3]),
-        "=&v"(pk.v[2][0]), "=&v"(pk.v[2][1]), "=&v"(pk.v[2][2]), "=&v"(pk.v[2][3]),
-        "=&v"(pk.v[3][0]), "=&v"(pk.v[3][1]), "=&v"(pk.v[3][2]), "=&v"(pk.v[3][3])
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "n"(N)
-      : "memory");
-  pk.s = 1.0f;
-}
 
 // Wait until at most n (<= 11) vector-memory operations are outstanding.
 __device__ __forceinline__ void wait_vm_n(int32_t n) {
