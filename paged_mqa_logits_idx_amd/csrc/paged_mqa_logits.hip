@@ -1145,12 +1145,19 @@ __device__ __forceinline__ uint32_t order_key(float v) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+// Inclusive prefix sum over the wave's 64 lanes with DPP moves (no LDS
+// round trips): shifts by 1, 2, 4, 8 within each row of 16 lanes, then the
+// row totals carried by row_bcast:15 (row r's last lane into row r+1, rows 1
+// and 3) and row_bcast:31 (lane 31 into rows 2 and 3).  Lanes with no source
+// add 0.
 __device__ __forceinline__ uint32_t wave_inclusive_scan_u32(uint32_t v, int lane) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t t = __shfl_up(v, d);
-    if (lane >= d) v += t;
-  }
+  (void)lane;
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, true);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, true);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, true);  // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false); // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false); // row_bcast:31
   return v;
 }
 
