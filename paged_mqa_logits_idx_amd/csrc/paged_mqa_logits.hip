@@ -1334,59 +1334,65 @@ __device__ __forceinline__ void topk_row(TopkShared<THREADS, CAP, CAND>& sh, con
 
   // Compaction: wave w owns positions [w*seg, (w+1)*seg), seg a multiple of
   // 256; lane l holds positions c0+4l .. c0+4l+3 of each 256-position step.
+  // Per lane and step the counts are packed (keys above the threshold in the
+  // low 16 bits, keys at it in the high 16; a step holds 256 positions), and
+  // one wave scan per step orders them; running totals are 32-bit.
   const int32_t seg = ((L + kWaves - 1) / kWaves + 255) & ~255;
   const int32_t s0 = min(wave * seg, L), s1 = min(s0 + seg, L);
-  uint32_t ng = 0u, nq = 0u;
-  for (int32_t c0 = s0; c0 < s1; c0 += 256) {
-    float v[4];
+  auto classify = [&](int32_t c0, float (&v)[4], uint32_t& bits) -> uint32_t {
     row4<RES>(sh, x, c0 + 4 * lane, s1, v);
+    uint32_t c = 0u;
+    bits = 0u;  // bit e: above, bit 4+e: at the threshold
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const bool ok = c0 + 4 * lane + e < s1;
       const uint32_t key = order_key(v[e]) & mask;
-      ng += (uint32_t)__builtin_popcountll(__ballot(ok && key > prefix));
-      nq += (uint32_t)__builtin_popcountll(__ballot(ok && key == prefix));
+      const uint32_t gt = (ok && key > prefix) ? 1u : 0u, eq = (ok && key == prefix) ? 1u : 0u;
+      c += gt | (eq << 16);
+      bits |= (gt << e) | (eq << (4 + e));
     }
+    return c;
+  };
+  uint32_t lane_g = 0u, lane_q = 0u;
+  for (int32_t c0 = s0; c0 < s1; c0 += 256) {
+    float v[4];
+    uint32_t bits;
+    const uint32_t c = classify(c0, v, bits);
+    lane_g += c & 0xFFFFu;
+    lane_q += c >> 16;
   }
+  const uint32_t wg = __builtin_amdgcn_readlane(wave_inclusive_scan_u32(lane_g, lane), 63);
+  const uint32_t wq = __builtin_amdgcn_readlane(wave_inclusive_scan_u32(lane_q, lane), 63);
   if (lane == 0) {
-    sh.wave_gt[wave] = ng;
-    sh.wave_eq[wave] = nq;
+    sh.wave_gt[wave] = wg;
+    sh.wave_eq[wave] = wq;
   }
   __syncthreads();
-  uint32_t g = 0u, q = 0u;
+  uint32_t g = 0u, q = 0u;  // candidates of the earlier waves' segments
   for (int w = 0; w < wave; ++w) {
     g += sh.wave_gt[w];
     q += sh.wave_eq[w];
   }
   for (int32_t c0 = s0; c0 < s1; c0 += 256) {
     float v[4];
-    row4<RES>(sh, x, c0 + 4 * lane, s1, v);
-    bool gt[4], eq[4];
-    uint64_t bg[4], be[4];
-    uint32_t gl = g, ql = q;
+    uint32_t bits;
+    const uint32_t c = classify(c0, v, bits);
+    const uint32_t incl = wave_inclusive_scan_u32(c, lane), ex = incl - c;
+    uint32_t gl = g + (ex & 0xFFFFu), ql = q + (ex >> 16);  // before this lane's first position
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const bool ok = c0 + 4 * lane + e < s1;
-      const uint32_t key = order_key(v[e]) & mask;
-      gt[e] = ok && key > prefix;
-      eq[e] = ok && key == prefix;
-      bg[e] = __ballot(gt[e]);
-      be[e] = __ballot(eq[e]);
-      gl += lanes_below(bg[e]);
-      ql += lanes_below(be[e]);
-      g += (uint32_t)__builtin_popcountll(bg[e]);
-      q += (uint32_t)__builtin_popcountll(be[e]);
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
+      const bool gt = (bits >> e) & 1u, eq = (bits >> (4 + e)) & 1u;
       const uint32_t slot = gl + min(ql, need);  // a key at the threshold: gl + ql when taken
-      if (gt[e] || (eq[e] && ql < need)) {
+      if (gt || (eq && ql < need)) {
         io[slot] = c0 + 4 * lane + e;
         if (vo) vo[slot] = v[e];
       }
-      gl += gt[e] ? 1u : 0u;
-      ql += eq[e] ? 1u : 0u;
+      gl += gt ? 1u : 0u;
+      ql += eq ? 1u : 0u;
     }
+    const uint32_t tot = __builtin_amdgcn_readlane(incl, 63);
+    g += tot & 0xFFFFu;
+    q += tot >> 16;
   }
   __syncthreads();  // wave_gt / wave_eq / vals / cand are rewritten by the next row
 }
