@@ -362,48 +362,6 @@ __device__ __forceinline__ int32_t wave_inclusive_scan(int32_t v, int lane) {
   return v;
 }
 
-// Live pages [ja, jb) of row b (0 <= ja < jb <= live pages of the row).  Keys
-// of the next NBUF-1 pages are in flight while the current page is multiplied
-// (buffers rotate; every index is a compile-time constant after unrolling).
-template <int KEY, int NBUF>
-__device__ __forceinline__ void row_pages(const Params& p, int32_t b, int32_t ja, int32_t jb,
-                                          int32_t L, int lane) {
-  RowQuery rq;
-  load_row_query(p, b, lane, rq);
-  const int32_t* tab = p.pt + (int64_t)b * p.pt_stride;
-  float* orow = p.out + (int64_t)b * p.width * kPage;
-  PageKeys<KEY> buf[NBUF];
-  bool ok[NBUF];
-#pragma unroll
-  for (int t = 0; t < NBUF - 1; ++t) {
-    ok[t] = false;
-    if (ja + t < jb) {
-      const int32_t g = load_uniform(tab, ja + t);
-      ok[t] = page_ok(g, p.num_pages);
-      if (ok[t]) load_page_global<KEY>(p, g, lane, buf[t]);
-    }
-  }
-  for (int32_t j = ja; j < jb; j += NBUF) {
-#pragma unroll
-    for (int u = 0; u < NBUF; ++u) {
-      const int32_t jj = j + u;
-      if (jj < jb) {
-        constexpr int kAhead = NBUF - 1;
-        const int nxt = (u + kAhead) % NBUF;
-        if (jj + kAhead < jb) {
-          const int32_t g = load_uniform(tab, jj + kAhead);
-          ok[nxt] = page_ok(g, p.num_pages);
-          if (ok[nxt]) load_page_global<KEY>(p, g, lane, buf[nxt]);
-        }
-        if (ok[u])
-          store_page(orow, jj, L, lane, score_page<KEY>(rq, buf[u], lane));
-        else
-          store_bad_page(orow, jj, L, lane);
-      }
-    }
-  }
-}
-
 // ---- fp8 pages streamed HBM -> LDS with global_load_lds_dwordx4 ----------
 // Each wave owns two LDS slots of 8448 bytes.  DMA instruction t (0..7) copies
 // the contiguous kilobyte of key rows 8t..8t+7 (lane l: row 8t + l/8, 16-byte
