@@ -375,3 +375,21 @@ def test_binding_rejects_bad_arguments(lib):
     st = lib.idx_paged_mqa_logits_fp8(q, kv, kv.data_ptr() + 8192, pt, sl, w, out, num_pages=1,
                                       check=False)
     assert st == -2
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_shapes(lib, seed):
+    """Seeded random problems: rows, width, pool, lengths (including <= 0 and
+    past the table), key format, table sharing and scale layout drawn per seed."""
+    rng = np.random.default_rng(900 + seed)
+    kind = ["fp8", "bf16"][seed % 2]
+    shared = bool(rng.integers(0, 2))
+    rows = int(rng.integers(1, 40))
+    width = int(rng.integers(1, 90))
+    pool = int(rng.integers(width, 3 * width + 2))
+    seq = rng.integers(-70, width * P + 140, size=rows)
+    layout = "split" if (kind == "fp8" and seed % 3 == 0) else "fused"
+    wl = W.random_workload(1200 + seed, kind, rows=rows, table_width=width, num_pages=pool,
+                           seqlens=seq, shared_table=shared, layout=layout)
+    st = check_full(lib, wl, label=f"random {seed}")
+    announce(f"random seed {seed} {kind} rows={rows} width={width} shared={shared} {layout}: {st}")

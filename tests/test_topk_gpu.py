@@ -72,7 +72,9 @@ def check_selection(lib, vals, seqlens, k, row_stride=None):
 @pytest.mark.parametrize("rows,ncols,k,kind", [
     (1, 8, 4, "special"), (9, 300, 1, "ties"), (9, 5000, 2048, "ties"), (9, 5000, 2048, "normal"),
     (9, 9000, 2048, "special"), (9, 4100, 2048, "equal"), (64, 40000, 2048, "normal"),
-    (9, 12288, 4096, "ties"), (9, 70000, 3, "normal")])
+    (9, 12288, 4096, "ties"), (9, 70000, 3, "normal"),
+    (5, 30000, 2048, "equal"),   # first digit holds more keys than the candidate list
+    (5, 6144, 700, "equal")])
 def test_topk_bit_exact(lib, rows, ncols, k, kind):
     rng = np.random.default_rng(rows * 7 + ncols + k)
     vals = values_of(rng, kind, rows, ncols)
