@@ -1,8 +1,8 @@
 """Benchmark of the paged MQA-logits indexer on one MI355X.
 
 Default workload: fp8 decode with a 4097-page table (262,208 c4-positions per
-row), 64 rows, lengths uniform in [512, 32768] -- the configuration on which the
-HBM-bandwidth target and the O(actual length) claim are judged.  One step = one
+row), 64 rows, lengths uniform in [512, 32768] -- the configuration that the
+HBM-bandwidth target and the O(actual length) claim refer to.  One step = one
 library call over the whole batch (grid/early exit, page lookup, key gather,
 fp8->bf16, MFMA, scale/ReLU/weighted head sum, masked store).
 
