@@ -252,7 +252,7 @@ def traffic_for(cfg_key: str, launches_alg_bytes: float):
         return None
     data = json.loads(TRAFFIC_FILE.read_text())
     ent = data.get(cfg_key)
-    if not ent or ent.get("kernel_sha") != kernel_sha():
+    if not ent or data.get("kernel_sha") != kernel_sha():
         return None
     return ent.get("bytes_per_launch")
 
