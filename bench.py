@@ -9,7 +9,10 @@ fp8->bf16, MFMA, scale/ReLU/weighted head sum, masked store).
 Prints ONE JSON line:
   value          c4-positions scored per second (live positions only), whole job
   roofline       HBM roofline of the kernel: algorithmic bytes per launch / mean
-                 launch time (HIP events on the launch stream) vs 8 TB/s
+                 launch time (HIP events on the launch stream) vs 8 TB/s, with the
+                 measured HBM traffic (rocprofv3 counters) and reachable
+                 denominators measured in the same run (a 1 GiB device copy, a
+                 bf16 8192^3 matrix product)
   cpu_baseline   the CPU oracle timed on a bounded row sample of the same workload
   secondary      same measurements for the 128-page decode, the 513-slot control
                  of the default workload, the bf16 prefill (MFMA roofline), the
@@ -176,6 +179,38 @@ def time_graph(step, steps: int, warmup: int):
     return ms, wall
 
 
+def achievable_peaks():
+    """Reachable denominators measured on this GPU: a 1 GiB device copy (HBM,
+    read + write bytes / time) and a 8192^3 bf16 matrix product through torch
+    (dense MFMA, hipBLASLt)."""
+    import torch
+
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    x = torch.randn((8192, 8192), device="cuda").to(torch.bfloat16)
+    y = torch.randn((8192, 8192), device="cuda").to(torch.bfloat16)
+    z = x @ y
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(5):
+        b.copy_(a)
+    e.record()
+    torch.cuda.synchronize()
+    copy_gbs = 5 * 2 * n / (s.elapsed_time(e) * 1e-3) / 1e9
+    s.record()
+    for _ in range(5):
+        z = x @ y
+    e.record()
+    torch.cuda.synchronize()
+    mm_tflops = 5 * 2 * 8192 ** 3 / (s.elapsed_time(e) * 1e-3) / 1e12
+    del a, b, x, y, z
+    torch.cuda.empty_cache()
+    return round(copy_gbs, 1), round(mm_tflops, 1)
+
+
 def measure_store(steps: int, warmup: int):
     """fp8 key store: every slot of the 32,768-page pool (2,097,152 keys) per step.
 
@@ -292,6 +327,8 @@ def main() -> int:
     cfg = args.workload if args.workload == "3c" else int(args.workload)
     wl, main_res = measure(cfg, args.steps, args.warmup)
     log(json.dumps(main_res))
+    copy_gbs, mm_tflops = achievable_peaks()
+    log(f"achievable: device copy {copy_gbs} GB/s, bf16 8192^3 matmul {mm_tflops} TFLOP/s")
 
     secondary = {}
     if not args.no_secondary:
@@ -308,10 +345,12 @@ def main() -> int:
                 entry.update(bound="mfma", achieved_tflops=round(r["tflops"], 2),
                              peak_tflops=BF16_MFMA_PEAK_TFLOPS,
                              frac=round(r["tflops"] / BF16_MFMA_PEAK_TFLOPS, 4),
+                             frac_of_matmul=round(r["tflops"] / mm_tflops, 4),
                              alg_flops=r["alg_flops"])
             else:
                 entry.update(bound="hbm", achieved_gbs=round(r["gbs"], 1), peak_gbs=HBM_PEAK_GBS,
                              frac=round(r["gbs"] / HBM_PEAK_GBS, 4),
+                             frac_of_copy=round(r["gbs"] / copy_gbs, 4),
                              alg_bytes=r["alg_read_bytes"] + r["alg_write_bytes"])
             secondary[str(c)] = entry
         for c in (cfg, 4):
@@ -324,6 +363,7 @@ def main() -> int:
                 "positions_per_s": r["positions_per_s_kernel"],
             }
         r = measure_store(max(10, args.steps // 2), max(3, args.warmup // 2))
+        r["frac_of_copy"] = round(r["achieved_gbs"] / copy_gbs, 4)
         log(json.dumps(r))
         secondary["store_fp8"] = r
 
@@ -372,6 +412,8 @@ def main() -> int:
             "traffic": traffic,
             "alg_bytes_per_launch": alg_bytes,
             "kernel_ms_mean": round(main_res["kernel_ms_mean"], 5),
+            "achievable": {"device_copy_gbs": copy_gbs, "frac_of_copy": round(achieved / copy_gbs, 4),
+                           "bf16_matmul_tflops": mm_tflops},
         },
         "cpu_baseline": cpu,
         "secondary": secondary,
