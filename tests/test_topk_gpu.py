@@ -39,6 +39,12 @@ def values_of(rng, kind, rows, ncols):
         v = np.full((rows, ncols), 1.5, dtype=np.float32)
         v[:, ::97] = 2.0
         return v
+    if kind in ("sample_low", "sample_high"):
+        # every 8th position far below / above the rest: a guess taken from
+        # those positions alone misplaces the k-th value (or finds it there)
+        v = (rng.standard_normal((rows, ncols)) * 7).astype(np.float32)
+        v[:, ::8] = -1000.0 if kind == "sample_low" else 1000.0
+        return v
     pool = np.array([0.0, -0.0, 1.0, -1.0, 2.5, np.nan, np.inf, -np.inf, 3.0e38, -1e-45],
                     dtype=np.float32)
     return pool[rng.integers(0, len(pool), size=(rows, ncols))]
@@ -74,7 +80,8 @@ def check_selection(lib, vals, seqlens, k, row_stride=None):
     (9, 9000, 2048, "special"), (9, 4100, 2048, "equal"), (64, 40000, 2048, "normal"),
     (9, 12288, 4096, "ties"), (9, 70000, 3, "normal"),
     (5, 30000, 2048, "equal"),   # first digit holds more keys than the candidate list
-    (5, 6144, 700, "equal")])
+    (5, 6144, 700, "equal"), (6, 20000, 2048, "sample_low"), (6, 20000, 2048, "sample_high"),
+    (6, 5000, 2048, "sample_low"), (6, 5000, 300, "sample_high")])
 def test_topk_bit_exact(lib, rows, ncols, k, kind):
     rng = np.random.default_rng(rows * 7 + ncols + k)
     vals = values_of(rng, kind, rows, ncols)
