@@ -40,6 +40,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "paged_mqa_logits.h"
 
 namespace {
@@ -1416,16 +1418,16 @@ constexpr int kBalancedSlots = 2;  // fp8 pages in flight per wave (LDS slots)
 
 // Compute units of the current device (queried once per device).
 int device_cu_count() {
-  static int cache[64];
+  static std::atomic<int> cache[64];  // per device; concurrent callers store the same value
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] <= 0) {
-    int n = 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       n = 256;
-    cache[dev] = n;
+    cache[dev].store(n, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return n;
 }
 
 inline bool aligned(const void* ptr, uintptr_t a) { return ((uintptr_t)ptr & (a - 1)) == 0; }
