@@ -53,8 +53,16 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_sha() -> str:
-    return hashlib.sha256(KERNEL_SOURCE.read_bytes()).hexdigest()[:16]
+def kernel_sha(source: Path = KERNEL_SOURCE) -> str:
+    """Hash of the kernel source's code: comments and blank space removed, so
+    that measured counters stay attached to the code they were taken on."""
+    import re
+
+    text = source.read_text()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = " ".join(text.split())
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
 def algorithmic_work(wl):

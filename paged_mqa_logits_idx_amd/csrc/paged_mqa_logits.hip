@@ -15,11 +15,14 @@
 // Context-Length Tax Vanished: Committing the O(actual) Triton Indexer",
 // section "The Commit: Engineering as Narrative").
 //
-// Two kernels share that per-page core:
-//  * rowwise  -- rows with their own page tables (decode).  Each wave owns a run
-//    of page slots of one row, keeps the row's query in registers across them
-//    and streams key bytes from HBM straight into the MFMA operand layout,
-//    prefetching the next page while the current one is multiplied.
+// Three kernels share that per-page core:
+//  * balanced -- rows with their own page tables (decode, up to 1024 rows).  A
+//    fixed grid whose waves take equal shares of all rows' live pages and of
+//    the -inf slots; each wave keeps its row's query in registers and streams
+//    pages HBM -> LDS by DMA, the next pages in flight while one is multiplied.
+//  * rowwise  -- rows with their own page tables beyond 1024 rows.  Each wave
+//    owns a run of page slots of one row and streams key bytes from HBM
+//    straight into the MFMA operand layout, one page ahead.
 //  * shared   -- rows that share page tables: the query tokens of one
 //    prefill request (page_table_row_stride == 0), or of several requests
 //    with a row -> request table map.  A workgroup owns 4 rows x a chunk of
@@ -28,6 +31,8 @@
 //    key bytes are fetched once per 4 rows and the query stays in registers
 //    for the chunk.  A block of 4 rows that straddles requests runs once per
 //    table.
+// Beside them: the paged key store (quantise / copy keys into pool slots) and
+// the top-k over logits rows.
 //
 // MFMA fragment layout (16x16x32 bf16, lane l, n = l % 16, g = l / 16):
 //   A (query)  row  h = 16*mb + n,  8 k-values,
@@ -854,11 +859,13 @@ __device__ __forceinline__ void read_shared_slot(uint32_t sb, int lane, PageKeys
   }
 }
 
-// Rows sharing one page table (page_table_row_stride == 0: the query tokens of
-// one prefill request).  Unit = (block of 4 rows, chunk of `chunk` page
-// slots); wave w scores row 4*rb + w.  Each page is copied once into LDS by
-// DMA -- kSharedSlots slots, pages kSharedSlots-1 ahead in flight -- and all 4
-// waves multiply it against their own row's query; one barrier per page.
+// Rows sharing page tables (page_table_row_stride == 0: the query tokens of
+// one prefill request; MULTI: rows mapped to request tables by p.rt).  Unit =
+// (block of 4 rows, chunk of `chunk` page slots[, table group]); wave w scores
+// row 4*rb + w.  Each page is copied once into LDS by DMA -- kSharedSlots
+// slots, pages kSharedSlots-1 ahead in flight -- and the waves whose rows use
+// the unit's table multiply it against their own row's query; one barrier per
+// page.
 constexpr int kSharedSlots = 2;
 
 template <int KEY, bool MULTI>
@@ -1079,8 +1086,8 @@ __global__ __launch_bounds__(64 * kStoreWaves) void store_keys_kernel(const uint
 // above T is taken).  An order-preserving compaction then writes candidate p
 // to slot (#keys > T before p) + min(#keys == T before p, need): each wave
 // owns a contiguous segment of the row, 4 positions per lane and 256 per
-// step, counts its candidates with ballots and emits them after a prefix
-// over the waves' counts.
+// step, counts its candidates per lane, and emits them after a prefix over
+// the waves' counts and one wave scan per step.
 // A row of at most CAP candidates is staged once in LDS (by DMA) and every
 // pass reads it there; after the first digit, the keys that share it (at
 // most CAND of them) are gathered into a list that the later digits scan
