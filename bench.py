@@ -281,12 +281,33 @@ def cpu_baseline(wl, target_s: float):
         ora.paged_mqa_logits(wl, rows=rows)
         el += time.perf_counter() - t
         reps += 1
+    threads = ora.num_threads()
+    # one thread, on the first sampled row only (a few seconds)
+    ora.set_num_threads(1)
+    try:
+        t = time.perf_counter()
+        ora.paged_mqa_logits(wl, rows=rows[:1])
+        one = time.perf_counter() - t
+    finally:
+        ora.set_num_threads(threads)
     return {
-        "value": acc * reps / el, "unit": "c4-positions/s", "cores": ora.num_threads(),
+        "value": acc * reps / el, "unit": "c4-positions/s", "cores": threads,
         "kind": "oracle",
         "sample": f"{len(rows)} of {wl.rows} rows of the default workload ({acc} live "
                   f"positions, float64) x {reps} runs, {el:.1f} s",
+        "one_thread_value": int(L[rows[0]]) / one if one > 0 else None,
+        "cpu_model": cpu_model(),
     }
+
+
+def cpu_model() -> str | None:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def traffic_for(cfg_key: str, launches_alg_bytes: float):
