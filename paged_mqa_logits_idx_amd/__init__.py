@@ -5,7 +5,7 @@ HIP kernels.  The functions carry the C-ABI names and argument order; they
 accept torch device tensors (or raw device addresses as ints) and pass their
 addresses and sizes through ctypes.  torch supplies device memory and streams.
 
-The library must be built in-tree first (``python -m paged_mqa_logits_idx_amd._build``
+The library must be built in-tree first (``python paged_mqa_logits_idx_amd/_build.py``
 or ``__graft_entry__.build()``); importing this module without it raises.
 """
 from __future__ import annotations
@@ -57,7 +57,7 @@ def _load() -> ctypes.CDLL:
     if not LIB_PATH.exists():
         raise ImportError(
             f"{LIB_PATH} is missing: build the HIP library first "
-            "(python -m paged_mqa_logits_idx_amd._build)")
+            "(python paged_mqa_logits_idx_amd/_build.py)")
     lib = ctypes.CDLL(str(LIB_PATH))
     argtypes = [
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
