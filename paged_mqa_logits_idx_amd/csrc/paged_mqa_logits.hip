@@ -288,6 +288,41 @@ __device__ __forceinline__ int32_t load_uniform(const int32_t* base, int64_t idx
   return ((const_i32)(uintptr_t)base)[uniform(idx)];
 }
 
+// Logits of a row segment's live pages wait in a per-wave LDS buffer and go
+// to memory in runs of up to kScoreBufPages pages (16-byte stores), at the end
+// of the segment or when the buffer is full.  Vector-memory operations retire
+// in issue order, so a store issued between two page DMAs makes the wait for
+// the later page also wait for that store's acknowledgement; buffered, the
+// stores issue after the segment's last DMA.
+constexpr int kScoreBufPages = 12;  // 3 KiB of LDS per wave
+typedef __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+
+struct ScoreBuffer {
+  lds_f32* buf;  // [kScoreBufPages][64]
+  float* orow;   // output row
+  int32_t j0;    // page slot of buf[0]
+  int32_t n;     // pages held
+};
+
+__device__ __forceinline__ void score_buffer_flush(ScoreBuffer& sb, int lane) {
+  const lds_f32x4* src = reinterpret_cast<const lds_f32x4*>(sb.buf);
+  f32x4* dst = reinterpret_cast<f32x4*>(sb.orow + (int64_t)sb.j0 * kPage);
+  for (int32_t i = lane; i < sb.n * (kPage / 4); i += 64) __builtin_nontemporal_store(src[i], dst + i);
+  sb.j0 = uniform(sb.j0 + sb.n);
+  sb.n = 0;
+}
+
+// Logit v of position 64*j + lane (NaN for a page id outside the pool), -inf
+// from the row length L on.
+__device__ __forceinline__ void score_buffer_put(ScoreBuffer& sb, bool page_valid, float v, int32_t L,
+                                                 int lane) {
+  const int32_t pos = (sb.j0 + sb.n) * kPage + lane;
+  sb.buf[sb.n * kPage + lane] = pos < L ? (page_valid ? v : __builtin_nanf("")) : -INFINITY;
+  sb.n = uniform(sb.n + 1);
+  if (sb.n == kScoreBufPages) score_buffer_flush(sb, lane);
+}
+
 // ---------------------------------------------------------------------------
 // rowwise kernel: unit = (row b, WAVES*PPW consecutive page slots); wave w of
 // the unit owns PPW slots.
@@ -583,11 +618,11 @@ __device__ __forceinline__ void dma_page_bf16(const uint8_t* keys, lds_u8* slot,
 // is requested as soon as page t is in registers, and flies while page t is
 // multiplied.
 __device__ __forceinline__ void row_pages_dma_bf16(const Params& p, int32_t b, int32_t ja, int32_t jb,
-                                                   int32_t L, int lane, lds_u8* slot) {
+                                                   int32_t L, int lane, lds_u8* slot, lds_f32* sbuf) {
   RowQuery rq;
   load_row_query(p, b, lane, rq);
   const int32_t* tab = p.pt + (int64_t)b * p.pt_stride;
-  float* orow = p.out + (int64_t)b * p.width * kPage;
+  ScoreBuffer out{sbuf, p.out + (int64_t)b * p.width * kPage, ja, 0};
   // A page id outside the pool is never dereferenced: its DMA reads the row's
   // own query (16 KiB, always valid memory) and its logits become NaN.
   const uint8_t* safe = p.q + (int64_t)b * (kHeads * kDim * 2);
@@ -601,12 +636,10 @@ __device__ __forceinline__ void row_pages_dma_bf16(const Params& p, int32_t b, i
   const uint32_t sb = (uint32_t)(uintptr_t)slot;
   int32_t g_ahead = (1 < J) ? load_uniform(tab, ja + 1) : -1;
   for (int32_t tt = 0; tt < J; ++tt) {
-    // Operations issued after page tt's DMA: the store of iteration tt-1.
+    // Page tt's DMA is the newest operation (apart from the stores of a
+    // buffer flush, which this wait then also covers).
     PageKeys<kBf16> pk;
-    if (tt == 0)
-      read_slot_bf16<0>(sb, lane, pk);
-    else
-      read_slot_bf16<1>(sb, lane, pk);
+    read_slot_bf16<0>(sb, lane, pk);
     const bool cur_ok = ok;
     const int32_t g = g_ahead;
     g_ahead = (tt + 2 < J) ? load_uniform(tab, ja + tt + 2) : -1;
@@ -614,22 +647,20 @@ __device__ __forceinline__ void row_pages_dma_bf16(const Params& p, int32_t b, i
       ok = page_ok(g, p.num_pages);
       dma_page_bf16(ok ? p.kv + (int64_t)g * p.kv_stride : safe, slot, lane);
     }
-    if (cur_ok)
-      store_page(orow, ja + tt, L, lane, score_page<kBf16>(rq, pk, lane));
-    else
-      store_bad_page(orow, ja + tt, L, lane);
+    score_buffer_put(out, cur_ok, cur_ok ? score_page<kBf16>(rq, pk, lane) : 0.f, L, lane);
   }
+  score_buffer_flush(out, lane);
 }
 
 // Live pages [ja, jb) of row b through the wave's NS LDS slots: NS pages are
 // in flight while one is multiplied.
 template <int NS>
 __device__ __forceinline__ void row_pages_dma(const Params& p, int32_t b, int32_t ja, int32_t jb,
-                                              int32_t L, int lane, lds_u8* slots) {
+                                              int32_t L, int lane, lds_u8* slots, lds_f32* sbuf) {
   RowQuery rq;
   load_row_query(p, b, lane, rq);
   const int32_t* tab = p.pt + (int64_t)b * p.pt_stride;
-  float* orow = p.out + (int64_t)b * p.width * kPage;
+  ScoreBuffer out{sbuf, p.out + (int64_t)b * p.width * kPage, ja, 0};
   // A page id outside the pool is never dereferenced: its DMA reads the row's
   // own query bytes instead (always valid memory) and its logits become NaN.
   const uint8_t* safe = p.q + (int64_t)b * (kHeads * kDim * 2);
@@ -663,13 +694,13 @@ __device__ __forceinline__ void row_pages_dma(const Params& p, int32_t b, int32_
         const uint32_t a0 = base + u * kSlotBytes + off0;
         const uint32_t a1 = base + u * kSlotBytes + off1;
         const uint32_t a4 = base + u * kSlotBytes + 8192 + 4 * lane;
-        // Operations issued after page tt's DMA group: one store per earlier
-        // iteration since that group (min(tt, NS) of them) and the groups of
-        // the pages after it -- prologue groups for tt < NS, plus one group
-        // per iteration i in [tt-NS+1, tt-1] with i+NS < J.
+        // Operations issued after page tt's DMA group: the groups of the
+        // pages after it -- prologue groups for tt < NS, plus one group per
+        // iteration i in [tt-NS+1, tt-1] with i+NS < J.  (The stores of a
+        // buffer flush are not counted: the wait then also covers them.)
         const int32_t lo = max(0, tt - NS + 1), hi = min(tt - 1, J - NS - 1);
         const int32_t groups = (tt < NS ? NS - 1 - tt : 0) + max(0, hi - lo + 1);
-        const int32_t n_after = min(tt, NS) + kDmaOps * groups;
+        const int32_t n_after = kDmaOps * groups;
         PageKeys<kFp8> pk;
         read_slot_after(uniform(n_after), a0, a1, a4, pk);
         const bool cur_ok = ok[u];
@@ -681,13 +712,11 @@ __device__ __forceinline__ void row_pages_dma(const Params& p, int32_t b, int32_
           const uint8_t* sc = ok[u] ? p.ks + (int64_t)g * p.ks_stride : safe + 8192;
           dma_page(keys, sc, slot, lane);
         }
-        if (cur_ok)
-          store_page(orow, ja + tt, L, lane, score_page<kFp8>(rq, pk, lane));
-        else
-          store_bad_page(orow, ja + tt, L, lane);
+        score_buffer_put(out, cur_ok, cur_ok ? score_page<kFp8>(rq, pk, lane) : 0.f, L, lane);
       }
     }
   }
+  score_buffer_flush(out, lane);
 }
 
 // Live pages [s, e) of the row-major sequence of all rows' live pages.
@@ -722,9 +751,9 @@ __device__ __forceinline__ void live_share(const Params& p, int64_t s, int64_t e
     const int32_t jb = (int32_t)min<int64_t>(lp, e - excl);
     if (ja < jb) {
       if constexpr (KEY == kFp8)
-        row_pages_dma<NS>(p, r, ja, jb, L, lane, my_slots);
+        row_pages_dma<NS>(p, r, ja, jb, L, lane, my_slots, (lds_f32*)(my_slots + NS * kSlotBytes));
       else
-        row_pages_dma_bf16(p, r, ja, jb, L, lane, my_slots);
+        row_pages_dma_bf16(p, r, ja, jb, L, lane, my_slots, (lds_f32*)(my_slots + kBf16SlotBytes));
     }
     pos = uniform(excl + jb);
     excl = uniform(excl + lp);
@@ -739,7 +768,8 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
   const int64_t nw = (int64_t)gridDim.x * WAVES;
   const int64_t wid = (int64_t)blockIdx.x * WAVES + wave;
   const int32_t rows = p.rows, width = p.width;
-  constexpr int kWaveLds = (KEY == kFp8) ? NS * kSlotBytes : kBf16SlotBytes;  // per wave
+  // per wave: the DMA slots, then the logits buffer
+  constexpr int kWaveLds = ((KEY == kFp8) ? NS * kSlotBytes : kBf16SlotBytes) + kScoreBufPages * kPage * 4;
   __shared__ __attribute__((aligned(16))) uint8_t lds_raw[WAVES * kWaveLds];
   lds_u8* dma_slots = (lds_u8*)lds_raw;
 

@@ -363,6 +363,28 @@ def test_grid_stride_beyond_grid_cap(lib):
     assert_parity(got[sample], oracle.paged_mqa_logits(wl, rows=sample), m[sample])
 
 
+@pytest.mark.parametrize("kind", ["fp8", "bf16"])
+def test_long_live_shares(lib, kind):
+    """Enough live pages that each wave of the decode grid scores more pages
+    than its logits buffer holds (12), so the buffer is written out in the
+    middle of a row segment as well as at its end; segments also cross rows."""
+    rows, width = 64, 600
+    rng = np.random.default_rng(95)
+    seq = rng.integers(width * P - 2 * P, width * P + 1, size=rows)
+    seq[3] = 0                                          # an empty row between full ones
+    wl = W.random_workload(95, kind, rows=rows, table_width=width, num_pages=256,
+                           seqlens=seq, pad=-1)
+    assert wl.live_pages() > 12 * 4 * 512               # > 12 pages per wave at any grid
+    got = run(lib, wl)
+    m = mask_of(wl)
+    assert np.array_equal(np.isneginf(got), m)
+    assert np.isfinite(got[~m]).all()
+    sample = [0, 2, 3, 4, 31, 62, 63]
+    st = assert_parity(got[sample], oracle.paged_mqa_logits(wl, rows=sample), m[sample],
+                       label=f"long shares {kind}")
+    announce(f"long shares {kind}: {st}")
+
+
 def test_binding_rejects_bad_arguments(lib):
     q = torch.zeros((2, 32, D), dtype=torch.bfloat16, device="cuda")
     kv = torch.zeros(8448, dtype=torch.uint8, device="cuda")
