@@ -9,7 +9,10 @@
 // Work decomposition.  One wave (64 lanes) scores one 64-position page of one
 // row: a 64-head x 64-position x 128 contraction done as 64 MFMAs
 // v_mfma_f32_16x16x32_bf16, then the epilogue (scale, ReLU, head weights, sum
-// over heads) on the accumulators and one 256-byte store.  The grid is fixed by
+// over heads) on the accumulators, leaving one logit per lane.  The balanced
+// and shared kernels collect a run of pages' logits in LDS and store them
+// after the run's key DMAs; the rowwise kernel stores each page's 256 bytes at
+// once.  The grid is fixed by
 // (rows, table_width); a page that starts at or past the row length is written
 // as -inf without touching the page table or the cache ("The Moment the
 // Context-Length Tax Vanished: Committing the O(actual) Triton Indexer",
@@ -288,21 +291,23 @@ __device__ __forceinline__ int32_t load_uniform(const int32_t* base, int64_t idx
   return ((const_i32)(uintptr_t)base)[uniform(idx)];
 }
 
-// Logits of a row segment's live pages wait in a per-wave LDS buffer and go
-// to memory in runs of up to kScoreBufPages pages (16-byte stores), at the end
-// of the segment or when the buffer is full.  Vector-memory operations retire
-// in issue order, so a store issued between two page DMAs makes the wait for
-// the later page also wait for that store's acknowledgement; buffered, the
-// stores issue after the segment's last DMA.
-constexpr int kScoreBufPages = 12;  // 3 KiB of LDS per wave
+// Logits of a wave's consecutive pages of one row wait in a per-wave LDS
+// buffer and go to memory in runs of up to `cap` pages (16-byte stores), at
+// the end of the run or when the buffer is full.  Vector-memory operations
+// retire in issue order, so a store issued between two page DMAs makes the
+// wait for the later page also wait for that store's acknowledgement;
+// buffered, the stores issue after the run's last DMA.
+constexpr int kScoreBufPages = 12;        // decode: 3 KiB of LDS per wave
+constexpr int kSharedScoreBufPages = 24;  // prefill: 6 KiB of LDS per wave
 typedef __attribute__((address_space(3))) float lds_f32;
 typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 
 struct ScoreBuffer {
-  lds_f32* buf;  // [kScoreBufPages][64]
+  lds_f32* buf;  // [cap][64]
   float* orow;   // output row
   int32_t j0;    // page slot of buf[0]
   int32_t n;     // pages held
+  int32_t cap;   // pages the buffer holds
 };
 
 __device__ __forceinline__ void score_buffer_flush(ScoreBuffer& sb, int lane) {
@@ -320,7 +325,7 @@ __device__ __forceinline__ void score_buffer_put(ScoreBuffer& sb, bool page_vali
   const int32_t pos = (sb.j0 + sb.n) * kPage + lane;
   sb.buf[sb.n * kPage + lane] = pos < L ? (page_valid ? v : __builtin_nanf("")) : -INFINITY;
   sb.n = uniform(sb.n + 1);
-  if (sb.n == kScoreBufPages) score_buffer_flush(sb, lane);
+  if (sb.n == sb.cap) score_buffer_flush(sb, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -622,7 +627,7 @@ __device__ __forceinline__ void row_pages_dma_bf16(const Params& p, int32_t b, i
   RowQuery rq;
   load_row_query(p, b, lane, rq);
   const int32_t* tab = p.pt + (int64_t)b * p.pt_stride;
-  ScoreBuffer out{sbuf, p.out + (int64_t)b * p.width * kPage, ja, 0};
+  ScoreBuffer out{sbuf, p.out + (int64_t)b * p.width * kPage, ja, 0, kScoreBufPages};
   // A page id outside the pool is never dereferenced: its DMA reads the row's
   // own query (16 KiB, always valid memory) and its logits become NaN.
   const uint8_t* safe = p.q + (int64_t)b * (kHeads * kDim * 2);
@@ -660,7 +665,7 @@ __device__ __forceinline__ void row_pages_dma(const Params& p, int32_t b, int32_
   RowQuery rq;
   load_row_query(p, b, lane, rq);
   const int32_t* tab = p.pt + (int64_t)b * p.pt_stride;
-  ScoreBuffer out{sbuf, p.out + (int64_t)b * p.width * kPage, ja, 0};
+  ScoreBuffer out{sbuf, p.out + (int64_t)b * p.width * kPage, ja, 0, kScoreBufPages};
   // A page id outside the pool is never dereferenced: its DMA reads the row's
   // own query bytes instead (always valid memory) and its logits become NaN.
   const uint8_t* safe = p.q + (int64_t)b * (kHeads * kDim * 2);
@@ -905,13 +910,15 @@ __global__ __launch_bounds__(64 * kSharedRows) __attribute__((amdgpu_waves_per_e
                                                                   int64_t total_slots) {
   constexpr int NS = kSharedSlots;
   constexpr int kSlot = (KEY == kFp8) ? kSlotBytes : 16384;
-  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[NS * kSlot];
+  // page slots, then one logits buffer per wave
+  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[NS * kSlot + kSharedRows * kSharedScoreBufPages * kPage * 4];
   lds_u8* slots = (lds_u8*)lds_raw;
   const uint32_t base = (uint32_t)(uintptr_t)slots;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int32_t ops = shared_dma_ops<KEY>(wave);  // DMA operations per page
+  lds_f32* sbuf = (lds_f32*)(lds_raw + NS * kSlot + wave * kSharedScoreBufPages * kPage * 4);
   const int32_t width = p.width;
 
   // MULTI: four groups per (row block, chunk) unit, the group index slowest
@@ -991,13 +998,14 @@ __global__ __launch_bounds__(64 * kSharedRows) __attribute__((amdgpu_waves_per_e
         // (Wave 0 of the fp8 kernel has one more operation per page; waiting on
         // the smaller count there costs it a part of page 0, no more.)
         __builtin_amdgcn_s_waitcnt(wait_vm((NS - 1) * shared_dma_ops<KEY>(1)));
-        const int32_t st = row_ok ? 1 : 0;  // stores per iteration
+        ScoreBuffer logits{sbuf, orow, j0, 0, kSharedScoreBufPages};
         for (int32_t t = 0; j0 + t < jl; ++t) {
           const int32_t j = j0 + t;
           const int u = t % NS;
           // Operations issued after page t's DMA: the pages of the (NS-2) later
-          // DMAs and the stores of the min(t, NS-1) iterations since it.
-          const int32_t n_after = uniform(min(t, NS - 1) * st + (NS - 2) * ops);
+          // DMAs (the stores of a buffer flush are not counted: the wait then
+          // also covers them).
+          const int32_t n_after = uniform((NS - 2) * ops);
           // Every wave waits for its own part of page t; the barrier then makes
           // the whole page visible -- and also guarantees that every wave is
           // done with slot (t-1) % NS, which the next DMA overwrites.
@@ -1006,16 +1014,13 @@ __global__ __launch_bounds__(64 * kSharedRows) __attribute__((amdgpu_waves_per_e
           PageKeys<KEY> pk;
           if (row_ok && j < live_w) read_shared_slot<KEY>(base + (uint32_t)(u * kSlot), lane, pk);
           issue(t + NS - 1);
-          if (row_ok) {
-            if (j >= live_w) {
-              store_page(orow, j, 0, lane, 0.f);  // whole page past this row's length
-            } else if ((ok_bits >> u) & 1u) {
-              store_page(orow, j, L, lane, score_page<KEY>(rq, pk, lane));
-            } else {
-              store_bad_page(orow, j, L, lane);
-            }
+          if (row_ok) {  // (a page past this row's length is all -inf)
+            const bool valid = (ok_bits >> u) & 1u;
+            score_buffer_put(logits, valid, (j < live_w && valid) ? score_page<KEY>(rq, pk, lane) : 0.f,
+                             L, lane);
           }
         }
+        if (row_ok) score_buffer_flush(logits, lane);
         __builtin_amdgcn_s_waitcnt(wait_vm(0));
         __builtin_amdgcn_s_barrier();  // LDS is reused by this workgroup's next unit
       }
