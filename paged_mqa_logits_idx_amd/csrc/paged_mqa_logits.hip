@@ -981,9 +981,14 @@ __global__ __launch_bounds__(64 * kSharedRows) __attribute__((amdgpu_waves_per_e
         // the operation count per iteration constant -- is copied from the
         // query buffer instead (always valid memory, at least 16 KiB).
         uint32_t ok_bits = 0;  // bit t % NS: page j0 + t has a valid id
-        auto issue = [&](int32_t t) {
+        // Table entry of page j0 + t (-1 past the pages any row needs).  Read
+        // one iteration before its DMA is issued, so that the scalar load's
+        // latency is not on the page loop's path.
+        auto table_entry = [&](int32_t t) -> int32_t {
           const int32_t j = j0 + t;
-          const int32_t g = (j < jl && table_ok) ? load_uniform(tab, j) : -1;
+          return (j < jl && table_ok) ? load_uniform(tab, j) : -1;
+        };
+        auto issue = [&](int32_t t, int32_t g) {
           const bool ok = page_ok(g, p.num_pages);
           const int u = t % NS;
           ok_bits = (uint32_t)uniform((int32_t)((ok_bits & ~(1u << u)) | ((ok ? 1u : 0u) << u)));
@@ -992,7 +997,8 @@ __global__ __launch_bounds__(64 * kSharedRows) __attribute__((amdgpu_waves_per_e
           shared_dma_page<KEY>(page, sc, slots + u * kSlot, wave, lane);
         };
 #pragma unroll
-        for (int t = 0; t < NS - 1; ++t) issue(t);
+        for (int t = 0; t < NS - 1; ++t) issue(t, table_entry(t));
+        int32_t g_next = table_entry(NS - 1);
         // The query was requested before these DMAs: wait for it here with them
         // still in flight, so that no conservative wait lands in the page loop.
         // (Wave 0 of the fp8 kernel has one more operation per page; waiting on
@@ -1013,7 +1019,8 @@ __global__ __launch_bounds__(64 * kSharedRows) __attribute__((amdgpu_waves_per_e
           __builtin_amdgcn_s_barrier();
           PageKeys<KEY> pk;
           if (row_ok && j < live_w) read_shared_slot<KEY>(base + (uint32_t)(u * kSlot), lane, pk);
-          issue(t + NS - 1);
+          issue(t + NS - 1, g_next);
+          g_next = table_entry(t + NS);
           if (row_ok) {  // (a page past this row's length is all -inf)
             const bool valid = (ok_bits >> u) & 1u;
             score_buffer_put(logits, valid, (j < live_w && valid) ? score_page<KEY>(rq, pk, lane) : 0.f,
