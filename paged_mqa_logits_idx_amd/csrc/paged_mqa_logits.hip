@@ -883,14 +883,31 @@ __device__ __forceinline__ void wait_vm_n(int32_t n) {
   }
 }
 
-// Page of a slot whose DMA is known complete (the wait count 63 is no wait).
+// Page of a slot whose DMA is complete, through LDS loads the compiler sees
+// (same fragment layout as read_slot / read_slot_bf16).  Used where no DMA is
+// in flight when the page is read, so the compiler adds no wait for one; it
+// waits for each fragment only where an MFMA first needs it, and the loads
+// overlap the next page's DMA issue.
+typedef __attribute__((address_space(3))) const u32x4 lds_u32x4c;
+typedef __attribute__((address_space(3))) const float lds_f32c;
 template <int KEY>
 __device__ __forceinline__ void read_shared_slot(uint32_t sb, int lane, PageKeys<KEY>& pk) {
   if constexpr (KEY == kBf16) {
-    read_slot_bf16<63>(sb, lane, pk);
+    const int n = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        pk.v[nb][v] = *(lds_u32x4c*)(size_t)(sb + (uint32_t)(n * 256 + 16 * ((4 * g + v) ^ n)) + 4096 * nb);
+    pk.s = 1.0f;
   } else {
     const uint32_t a0 = sb + slot_chunk_offset(lane, 0), a1 = sb + slot_chunk_offset(lane, 1);
-    read_slot<63>(a0, a1, sb + 8192 + 4 * lane, pk);
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      pk.v[nb][0] = *(lds_u32x4c*)(size_t)(a0 + 2048 * nb);
+      pk.v[nb][1] = *(lds_u32x4c*)(size_t)(a1 + 2048 * nb);
+    }
+    pk.s = *(lds_f32c*)(size_t)(sb + 8192 + 4 * lane);
   }
 }
 
@@ -901,10 +918,10 @@ __device__ __forceinline__ void read_shared_slot(uint32_t sb, int lane, PageKeys
 // slots, pages kSharedSlots-1 ahead in flight -- and the waves whose rows use
 // the unit's table multiply it against their own row's query; one barrier per
 // page.
-constexpr int kSharedSlots = 2;
+constexpr int kSharedSlots = 2;  // (read_shared_slot relies on no DMA in flight at the read)
 
 template <int KEY, bool MULTI>
-__global__ __launch_bounds__(64 * kSharedRows) __attribute__((amdgpu_waves_per_eu(MULTI ? 2 : 1))) void shared_kernel(Params p, int32_t row_blocks,
+__global__ __launch_bounds__(64 * kSharedRows) __attribute__((amdgpu_waves_per_eu(2, 2))) void shared_kernel(Params p, int32_t row_blocks,
                                                                   int32_t chunk, int32_t chunks,
                                                                   int32_t rb_per_xcd,
                                                                   int64_t total_slots) {
@@ -1014,9 +1031,14 @@ __global__ __launch_bounds__(64 * kSharedRows) __attribute__((amdgpu_waves_per_e
           const int32_t n_after = uniform((NS - 2) * ops);
           // Every wave waits for its own part of page t; the barrier then makes
           // the whole page visible -- and also guarantees that every wave is
-          // done with slot (t-1) % NS, which the next DMA overwrites.
+          // done with slot (t-1) % NS, which the next DMA overwrites (the
+          // release fence waits for this wave's reads of it).  The acquire
+          // fence keeps the page's LDS loads after the barrier.  With two
+          // slots no DMA is in flight here (n_after is 0).
           wait_vm_n(n_after);
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
           __builtin_amdgcn_s_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
           PageKeys<KEY> pk;
           if (row_ok && j < live_w) read_shared_slot<KEY>(base + (uint32_t)(u * kSlot), lane, pk);
           issue(t + NS - 1, g_next);
