@@ -423,6 +423,11 @@ __device__ __forceinline__ int32_t wave_inclusive_scan(int32_t v, int lane) {
 // holding them in VGPRs.
 constexpr int kSlotBytes = 8448;
 constexpr int kDmaOps = 9;  // VMEM instructions per page (8 x 16 B + 1 x 4 B)
+// Cache policy of the decode key DMAs: non-temporal.  In decode every key byte
+// is read once per launch, so the pages stream past the L2 and the last-level
+// cache instead of displacing lines that are reused (queries, tables, the
+// output).  Measured on the 4097-wide decode: 41.2 -> 37.2 us.
+constexpr int kDmaStreaming = 2;  // the nt bit of the load's cache-policy operand
 // s_waitcnt immediate (gfx9 layout: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] |
 // vmcnt[5:4] << 14) waiting on vmcnt only.
 constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
@@ -434,9 +439,10 @@ __device__ __forceinline__ void dma_page(const uint8_t* keys, const uint8_t* sca
   for (int t = 0; t < 8; ++t) {
     const int i = 8 * t + rsub;
     const uint8_t* src = keys + i * kDim + 16 * (c ^ (i & 7));
-    __builtin_amdgcn_global_load_lds((global_ptr)src, (lds_ptr)(slot + 1024 * t), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((global_ptr)src, (lds_ptr)(slot + 1024 * t), 16, 0, kDmaStreaming);
   }
-  __builtin_amdgcn_global_load_lds((global_ptr)(scales + 4 * lane), (lds_ptr)(slot + 8192), 4, 0, 0);
+  __builtin_amdgcn_global_load_lds((global_ptr)(scales + 4 * lane), (lds_ptr)(slot + 8192), 4, 0,
+                                   kDmaStreaming);
 }
 
 // Lane's LDS byte offsets (within a slot) of its two 16-byte B chunks of
@@ -615,7 +621,7 @@ __device__ __forceinline__ void dma_page_bf16(const uint8_t* keys, lds_u8* slot,
   for (int t = 0; t < kBf16DmaOps; ++t) {
     const int i = 4 * t + r;
     __builtin_amdgcn_global_load_lds((global_ptr)(keys + i * 256 + 16 * (c ^ (i & 15))),
-                                     (lds_ptr)(slot + 1024 * t), 16, 0, 0);
+                                     (lds_ptr)(slot + 1024 * t), 16, 0, kDmaStreaming);
   }
 }
 
