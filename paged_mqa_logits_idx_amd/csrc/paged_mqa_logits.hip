@@ -791,13 +791,19 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
     if (r < rows) acc += live_pages_of(clamp_len(p.sl[r], width));
   }
   const int64_t total = uniform(wave_sum(acc));
-  // Waves of the grid's first half write their -inf share before their pages
-  // and reach the key stream late; those of the second half start on the
-  // pages at once and write their share at the end, where they finish last.
-  // Weighing the first half's live share 3:2 evens the finish (measured: the
-  // 4097-wide decode 42.0 -> 41.2 us).
+  // Waves of the grid's first half write their -inf share before their pages;
+  // those of the second half start on the pages at once and write their share
+  // at the end.  The first half's live share is weighted up so that both
+  // halves finish together: 2:1 when the -inf bytes are at least a quarter of
+  // the live key bytes, 4:1 when they are fewer (measured on one box: the
+  // 4097-wide decode 37.7 us at 3:2, 36.8 at 2:1, 40.1 at 3:1; its 513-wide
+  // control 32.9 at 3:2, 31.7 at 4:1; the 128-wide decode 16.2 at 3:2, 15.8
+  // at 4:1).
   const int64_t h = (int64_t)WAVES * ((gridDim.x + 1) / 2);  // first-half waves
-  const int64_t wa = p.fill ? 3 : 1, wb = p.fill ? 2 : 1;     // no -inf share: even split
+  const int64_t dead = (int64_t)rows * width - total;          // page slots written -inf
+  constexpr int64_t kLivePageBytes = (KEY == kFp8) ? kSlotBytes : kBf16SlotBytes;
+  const bool big_fill = 4 * dead * (kPage * 4) >= total * kLivePageBytes;
+  const int64_t wa = p.fill ? (big_fill ? 2 : 4) : 1, wb = 1;  // no -inf share: even split
   const int64_t s = share_bound(wid, nw, h, wa, wb, total), e = share_bound(wid + 1, nw, h, wa, wb, total);
   // (2) the -inf share: an equal share of the page slots.  Workgroups of the
   // grid's second half score first and write -inf after, those of the first
