@@ -385,6 +385,27 @@ def test_long_live_shares(lib, kind):
     announce(f"long shares {kind}: {st}")
 
 
+@pytest.mark.parametrize("kind", ["bf16", "fp8"])
+def test_prefill_row_blocks_past_resident_grid(lib, kind):
+    """A shared-table prefill with more 4-row blocks (725) than resident
+    workgroups and not a multiple of them: with bf16 keys the blocks are dealt in
+    passes (long and short blocks paired, the last pass partial); every row is
+    scored exactly once."""
+    rows, width = 2900, 24
+    t = np.arange(rows)
+    seq = (width * P * (t + 1) + rows - 1) // rows           # causal limits, 1 .. width*64
+    wl = W.random_workload(97, kind, rows=rows, table_width=width, num_pages=40,
+                           seqlens=seq, shared_table=True)
+    got = run(lib, wl)
+    m = mask_of(wl)
+    assert np.array_equal(np.isneginf(got), m)
+    assert np.isfinite(got[~m]).all()
+    sample = [0, 1, 3, 4, 511 * 4, 512 * 4 + 1, 724 * 4, 2047, 2048, rows - 1]
+    st = assert_parity(got[sample], oracle.paged_mqa_logits(wl, rows=sample), m[sample],
+                       label=f"prefill 725 blocks {kind}")
+    announce(f"prefill 725 row blocks {kind}: {st}")
+
+
 def test_binding_rejects_bad_arguments(lib):
     q = torch.zeros((2, 32, D), dtype=torch.bfloat16, device="cuda")
     kv = torch.zeros(8448, dtype=torch.uint8, device="cuda")
