@@ -324,8 +324,11 @@ def traffic_for(cfg_key: str, launches_alg_bytes: float):
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # 400 timed launches after 100 warm-up ones: on MI355X the per-launch time
+    # settles only after a few hundred back-to-back launches (50 after 10
+    # measured 38-39 us on the 4097-wide decode, 400 after 100 36.3-36.5 us)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="3",
                     help="configuration: 0-4, 3c, 2b, 4f or varlen (default 3)")
     ap.add_argument("--no-secondary", action="store_true")
