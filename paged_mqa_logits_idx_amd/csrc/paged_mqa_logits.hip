@@ -311,6 +311,9 @@ struct ScoreBuffer {
 };
 
 __device__ __forceinline__ void score_buffer_flush(ScoreBuffer& sb, int lane) {
+  // The 16-byte reads below take values other lanes wrote as floats: keep
+  // them after those writes (a wave's LDS operations execute in order).
+  __asm__ volatile("" ::: "memory");
   const lds_f32x4* src = reinterpret_cast<const lds_f32x4*>(sb.buf);
   f32x4* dst = reinterpret_cast<f32x4*>(sb.orow + (int64_t)sb.j0 * kPage);
   for (int32_t i = lane; i < sb.n * (kPage / 4); i += 64) __builtin_nontemporal_store(src[i], dst + i);
