@@ -90,6 +90,35 @@ def test_store_fp8_bit_exact(lib, n, num_pages, seed):
     assert np.array_equal(got, want)
 
 
+def test_store_fp8_scale_ranges_bit_exact(lib):
+    """Keys whose scale (amax/448) falls below 2^-60, inside [2^-60, 2^100] and
+    above 2^100 (largest bf16 magnitudes), and keys whose values are exact
+    fractions of their maximum (quotients on e4m3fn rounding ties): the codes
+    and scales equal the oracle's bytes."""
+    rng = np.random.default_rng(21)
+    n = 1536
+    k = rng.standard_normal((n, D), dtype=np.float32)
+    mags = np.array([1e-35, 1e-20, 1e-16, 1e-3, 1.0, 1e5, 1e29, 3e30, 1e34, 1e38], dtype=np.float32)
+    with np.errstate(over="ignore"):
+        k = np.clip(k * mags[rng.integers(0, len(mags), size=(n, 1))], -3.3e38, 3.3e38)
+    ties = rng.random(n) < 0.25                       # values = (m/256) * amax
+    amax = np.abs(k).max(axis=1, keepdims=True)
+    frac = rng.integers(-256, 257, size=(n, D)).astype(np.float32) / np.float32(256.0)
+    k[ties] = (frac * amax)[ties]
+    assert np.isfinite(k).all()
+    bits = torch.from_numpy(k).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    num_pages = 24
+    slots = rng.permutation(num_pages * P)[:n].astype(np.int64)
+    pool0 = rng.integers(0, 256, size=num_pages * FUSED, dtype=np.uint8)
+    got, _ = store_fp8(lib, bits, slots, num_pages, pool0)
+    codes, scales = oracle.quantize_keys_fp8(bits)
+    assert np.isfinite(scales).all()
+    assert (scales < 2.0 ** -60).any() and (scales > 2.0 ** 100).any()
+    want, _ = expected_pool(pool0, codes, scales, slots, num_pages, FUSED, ks_stride=FUSED,
+                            ks_offset=P * D)
+    assert np.array_equal(got, want)
+
+
 def test_store_fp8_split_layout(lib):
     rng = np.random.default_rng(11)
     n, num_pages = 700, 16
