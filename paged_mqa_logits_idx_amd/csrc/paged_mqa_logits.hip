@@ -1204,15 +1204,18 @@ __global__ __launch_bounds__(64 * kStoreWaves) void store_keys_kernel(const uint
 // step, counts its candidates per lane, and emits them after a prefix over
 // the waves' counts and one wave scan per step.
 // A row of at most CAP candidates is staged once in LDS (by DMA) and every
-// pass reads it there; after the first digit, the keys that share it (at
-// most CAND of them) are gathered into a list that the later digits scan
-// instead of the row.  A longer row is re-read from memory by each pass.
+// pass reads it there; after the first digit, one sweep over the waves'
+// segments counts each segment's keys above that digit and lists the
+// positions of the keys in it (at most CAND of them).  The later digits scan
+// the list instead of the row, and the segments' counts above and at the
+// final key come from those counts and the list, so the compaction reads the
+// row only once more.  A longer row is re-read from memory by each pass.
 constexpr int kTopkBins = 2048;
 
 template <int THREADS, int CAP, int CAND>
 struct TopkShared {
   float vals[CAP];       // the row, when it fits
-  uint32_t cand[CAND];   // keys sharing the first digit
+  uint32_t cand[CAND];   // positions of the keys sharing the first digit
   uint32_t hist[kTopkBins];
   uint32_t wave_gt[THREADS / 64], wave_eq[THREADS / 64];
   uint32_t pick[3];      // chosen digit, candidates in the digits above it, in it
@@ -1358,43 +1361,47 @@ __device__ __forceinline__ void topk_row(TopkShared<THREADS, CAP, CAND>& sh, con
   constexpr int kWaves = THREADS / 64;
   constexpr int kSteps = (CAP + 4 * THREADS - 1) / (4 * THREADS);  // staged 16-byte groups per thread
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // The compaction's segments: wave w owns positions [w*seg, (w+1)*seg), seg
+  // a multiple of 256 with kWaves * seg >= L.
+  const int32_t seg = ((L + kWaves - 1) / kWaves + 255) & ~255;
+  const int32_t s0 = min(wave * seg, L), s1 = min(s0 + seg, L);
   // Radix select.  Invariant: 1 <= need <= candidates matching (prefix, mask).
   uint32_t prefix = 0u, mask = 0u, need = (uint32_t)k;
   row_histogram<RES, THREADS, kSteps>(sh, x, L, 0, prefix, mask);
   uint32_t in_digit = radix_step(sh, 0, prefix, mask, need, wave, lane);
+  bool counted = false;  // sh.wave_gt / wave_eq hold the segments' counts
   if (need != in_digit) {
-    // Gather the keys of the first digit (RES rows whose digit fits the list).
+    // RES rows whose first digit fits the list: one sweep over this wave's
+    // segment counts the keys above the digit and lists the positions in it.
     const bool listed = RES && in_digit <= (uint32_t)CAND;
     if (listed) {
-      uint32_t hits = 0u, m = 0u;  // bit 4j+e: element (j, e) of this thread matches
+      uint32_t lane_g = 0u;
+      for (int32_t c0 = s0; c0 < s1; c0 += 256) {
+        float v[4];
+        row4<true>(sh, x, c0 + 4 * lane, s1, v);
+        uint32_t eqb = 0u;  // bit e: position c0 + 4*lane + e has the digit
 #pragma unroll
-      for (int j = 0; j < kSteps; ++j) {
-        const int32_t i = 4 * THREADS * j + 4 * tid;
-        if (i < L) {
-          float v[4];
-          row4<true>(sh, x, i, L, v);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const bool hit = i + e < L && (order_key(v[e]) & mask) == prefix;
-            hits |= (hit ? 1u : 0u) << (4 * j + e);
-          }
+        for (int e = 0; e < 4; ++e) {
+          const bool ok = c0 + 4 * lane + e < s1;
+          const uint32_t key = order_key(v[e]) & mask;
+          lane_g += (ok && key > prefix) ? 1u : 0u;
+          eqb |= (ok && key == prefix ? 1u : 0u) << e;
         }
-      }
-      m = __builtin_popcount(hits);
-      const uint32_t incl = wave_inclusive_scan_u32(m, lane);
-      uint32_t base = 0u;
-      if (lane == 63) base = atomicAdd(&sh.ncand, incl);
-      uint32_t at = __shfl(base, 63) + incl - m;
-#pragma unroll
-      for (int j = 0; j < kSteps; ++j) {
-        if ((hits >> (4 * j)) & 0xFu) {
-          const int32_t i = 4 * THREADS * j + 4 * tid;
-          float v[4];
-          row4<true>(sh, x, i, L, v);
+        if (__ballot(eqb != 0u)) {  // wave-uniform
+          const uint32_t m = __builtin_popcount(eqb);
+          const uint32_t incl = wave_inclusive_scan_u32(m, lane);
+          uint32_t base = 0u;
+          if (lane == 63) base = atomicAdd(&sh.ncand, incl);
+          uint32_t at = __shfl(base, 63) + incl - m;
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            if ((hits >> (4 * j + e)) & 1u) sh.cand[at++] = order_key(v[e]);
+            if ((eqb >> e) & 1u) sh.cand[at++] = (uint32_t)(c0 + 4 * lane + e);
         }
+      }
+      const uint32_t wg = __builtin_amdgcn_readlane(wave_inclusive_scan_u32(lane_g, lane), 63);
+      if (lane == 0) {
+        sh.wave_gt[wave] = wg;
+        sh.wave_eq[wave] = 0u;
       }
       __syncthreads();
     }
@@ -1403,7 +1410,7 @@ __device__ __forceinline__ void topk_row(TopkShared<THREADS, CAP, CAND>& sh, con
         const int shift = topk_shift(pass);
         const uint32_t dmask = topk_dmask(pass);
         for (int32_t i = tid; i < (int32_t)in_digit; i += THREADS) {
-          const uint32_t key = sh.cand[i];  // in_digit == the list's length
+          const uint32_t key = order_key(sh.vals[sh.cand[i]]);  // in_digit == the list's length
           if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & dmask], 1u);
         }
       } else {
@@ -1412,15 +1419,27 @@ __device__ __forceinline__ void topk_row(TopkShared<THREADS, CAP, CAND>& sh, con
       const uint32_t in_d = radix_step(sh, pass, prefix, mask, need, wave, lane);
       if (need == in_d) break;  // the whole digit is taken: no finer digit needed
     }
+    if (listed) {
+      // Keys outside the first digit are above the final key exactly when
+      // they are above the digit (counted); the listed ones are counted here
+      // into the segment that holds them.
+      for (int32_t i = tid; i < (int32_t)in_digit; i += THREADS) {
+        const uint32_t pos = sh.cand[i];
+        const uint32_t key = order_key(sh.vals[pos]) & mask;
+        const int w = (int)(pos / (uint32_t)seg);
+        if (key > prefix) atomicAdd(&sh.wave_gt[w], 1u);
+        else if (key == prefix) atomicAdd(&sh.wave_eq[w], 1u);
+      }
+      __syncthreads();
+      counted = true;
+    }
   }
 
-  // Compaction: wave w owns positions [w*seg, (w+1)*seg), seg a multiple of
-  // 256; lane l holds positions c0+4l .. c0+4l+3 of each 256-position step.
-  // Per lane and step the counts are packed (keys above the threshold in the
-  // low 16 bits, keys at it in the high 16; a step holds 256 positions), and
-  // one wave scan per step orders them; running totals are 32-bit.
-  const int32_t seg = ((L + kWaves - 1) / kWaves + 255) & ~255;
-  const int32_t s0 = min(wave * seg, L), s1 = min(s0 + seg, L);
+  // Compaction over the same segments; lane l holds positions c0+4l ..
+  // c0+4l+3 of each 256-position step.  Per lane and step the counts are
+  // packed (keys above the threshold in the low 16 bits, keys at it in the
+  // high 16; a step holds 256 positions), and one wave scan per step orders
+  // them; running totals are 32-bit.
   auto classify = [&](int32_t c0, float (&v)[4], uint32_t& bits) -> uint32_t {
     row4<RES>(sh, x, c0 + 4 * lane, s1, v);
     uint32_t c = 0u;
@@ -1435,21 +1454,23 @@ __device__ __forceinline__ void topk_row(TopkShared<THREADS, CAP, CAND>& sh, con
     }
     return c;
   };
-  uint32_t lane_g = 0u, lane_q = 0u;
-  for (int32_t c0 = s0; c0 < s1; c0 += 256) {
-    float v[4];
-    uint32_t bits;
-    const uint32_t c = classify(c0, v, bits);
-    lane_g += c & 0xFFFFu;
-    lane_q += c >> 16;
+  if (!counted) {
+    uint32_t lane_g = 0u, lane_q = 0u;
+    for (int32_t c0 = s0; c0 < s1; c0 += 256) {
+      float v[4];
+      uint32_t bits;
+      const uint32_t c = classify(c0, v, bits);
+      lane_g += c & 0xFFFFu;
+      lane_q += c >> 16;
+    }
+    const uint32_t wg = __builtin_amdgcn_readlane(wave_inclusive_scan_u32(lane_g, lane), 63);
+    const uint32_t wq = __builtin_amdgcn_readlane(wave_inclusive_scan_u32(lane_q, lane), 63);
+    if (lane == 0) {
+      sh.wave_gt[wave] = wg;
+      sh.wave_eq[wave] = wq;
+    }
+    __syncthreads();
   }
-  const uint32_t wg = __builtin_amdgcn_readlane(wave_inclusive_scan_u32(lane_g, lane), 63);
-  const uint32_t wq = __builtin_amdgcn_readlane(wave_inclusive_scan_u32(lane_q, lane), 63);
-  if (lane == 0) {
-    sh.wave_gt[wave] = wg;
-    sh.wave_eq[wave] = wq;
-  }
-  __syncthreads();
   uint32_t g = 0u, q = 0u;  // candidates of the earlier waves' segments
   for (int w = 0; w < wave; ++w) {
     g += sh.wave_gt[w];
