@@ -1204,17 +1204,20 @@ __global__ __launch_bounds__(64 * kStoreWaves) void store_keys_kernel(const uint
 // step, counts its candidates per lane, and emits them after a prefix over
 // the waves' counts and one wave scan per step.
 // A row of at most CAP candidates is staged once in LDS (by DMA) and every
-// pass reads it there; after the first digit, one sweep over the waves'
-// segments counts each segment's keys above that digit and lists the
-// positions of the keys in it (at most CAND of them).  The later digits scan
-// the list instead of the row, and the segments' counts above and at the
-// final key come from those counts and the list, so the compaction reads the
-// row only once more.  A longer row is re-read from memory by each pass.
+// pass reads it there; the first pass replaces each value by its order key,
+// so later passes read keys, and a selected value is its key inverted (read
+// again from the row only for NaN and zeros).  After the first digit, one
+// sweep over the waves' segments counts each segment's keys above that digit
+// and lists the positions of the keys in it (at most CAND of them).  The
+// later digits scan the list instead of the row, and the segments' counts
+// above and at the final key come from those counts and the list, so the
+// compaction reads the row only once more.  A longer row is re-read from
+// memory by each pass.
 constexpr int kTopkBins = 2048;
 
 template <int THREADS, int CAP, int CAND>
 struct TopkShared {
-  float vals[CAP];       // the row, when it fits
+  uint32_t vals[CAP];    // the staged row: its values' bits, then (from the first pass on) their order keys
   uint32_t cand[CAND];   // positions of the keys sharing the first digit
   uint32_t hist[kTopkBins];
   uint32_t wave_gt[THREADS / 64], wave_eq[THREADS / 64];
@@ -1266,19 +1269,33 @@ __device__ __forceinline__ void load4(const float* x, int32_t i, int32_t L, floa
   }
 }
 
+// Four consecutive order keys starting at i (a multiple of 4), 0 at or past
+// L.  RES: the staged row, which holds keys once the first pass has keyed it;
+// otherwise the values in memory, keyed here.
 template <bool RES, typename SH>
-__device__ __forceinline__ void row4(const SH& sh, const float* x, int32_t i, int32_t L, float (&v)[4]) {
+__device__ __forceinline__ void keys4(const SH& sh, const float* x, int32_t i, int32_t L, uint32_t (&kk)[4]) {
   if constexpr (RES) {
     if (i + 4 <= L) {
-      const f32x4 t = *reinterpret_cast<const f32x4*>(&sh.vals[i]);
-      v[0] = t[0]; v[1] = t[1]; v[2] = t[2]; v[3] = t[3];
+      const u32x4 t = *reinterpret_cast<const u32x4*>(&sh.vals[i]);
+      kk[0] = t[0]; kk[1] = t[1]; kk[2] = t[2]; kk[3] = t[3];
     } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = (i + e < L) ? sh.vals[i + e] : 0.0f;
+      for (int e = 0; e < 4; ++e) kk[e] = (i + e < L) ? sh.vals[i + e] : 0u;
     }
   } else {
+    float v[4];
     load4(x, i, L, v);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) kk[e] = order_key(v[e]);
   }
+}
+
+// The value of position pos of row x, given its order key: the key inverted,
+// or for the two keys that lose bits (0: NaN, any payload; 0x80000000: +0 or
+// -0) the value itself, read from the row.
+__device__ __forceinline__ float key_value(uint32_t key, const float* x, int32_t pos) {
+  if (key == 0u || key == 0x80000000u) return x[pos];
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
 }
 
 // Wave 0, once sh.hist holds this digit's counts over the candidates that
@@ -1327,20 +1344,34 @@ __device__ __forceinline__ uint32_t radix_step(SH& sh, int pass, uint32_t& prefi
   return sh.pick[2];
 }
 
-// Histogram of one digit over the row's keys that match (prefix, mask).
+// Histogram of one digit over the row's keys that match (prefix, mask).  The
+// first pass over a staged row replaces each value there by its order key.
 template <bool RES, int THREADS, int STEPS, typename SH>
 __device__ __forceinline__ void row_histogram(SH& sh, const float* x, int32_t L, int pass, uint32_t prefix,
                                               uint32_t mask) {
   const int shift = topk_shift(pass);
   const uint32_t dmask = topk_dmask(pass);
   auto count4 = [&](int32_t i) {
-    float v[4];
-    row4<RES>(sh, x, i, L, v);
+    uint32_t kk[4];
+    if (RES && pass == 0) {
+      if (i + 4 <= L) {
+        const u32x4 t = *reinterpret_cast<const u32x4*>(&sh.vals[i]);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t key = order_key(v[e]);
-      if (i + e < L && (key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & dmask], 1u);
+        for (int e = 0; e < 4; ++e) kk[e] = order_key(__uint_as_float(t[e]));
+        *reinterpret_cast<u32x4*>(&sh.vals[i]) = (u32x4){kk[0], kk[1], kk[2], kk[3]};
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kk[e] = (i + e < L) ? order_key(__uint_as_float(sh.vals[i + e])) : 0u;
+          if (i + e < L) sh.vals[i + e] = kk[e];
+        }
+      }
+    } else {
+      keys4<RES>(sh, x, i, L, kk);
     }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (i + e < L && (kk[e] & mask) == prefix) atomicAdd(&sh.hist[(kk[e] >> shift) & dmask], 1u);
   };
   const int tid = threadIdx.x;
   if constexpr (RES) {
@@ -1375,27 +1406,30 @@ __device__ __forceinline__ void topk_row(TopkShared<THREADS, CAP, CAND>& sh, con
     // segment counts the keys above the digit and lists the positions in it.
     const bool listed = RES && in_digit <= (uint32_t)CAND;
     if (listed) {
-      uint32_t lane_g = 0u;
-      for (int32_t c0 = s0; c0 < s1; c0 += 256) {
-        float v[4];
-        row4<true>(sh, x, c0 + 4 * lane, s1, v);
-        uint32_t eqb = 0u;  // bit e: position c0 + 4*lane + e has the digit
+      static_assert(4 * kSteps <= 32, "a lane's digit bits fill one word");
+      uint32_t lane_g = 0u, eqb = 0u;  // bit 4j+e: position s0 + 256j + 4*lane + e has the digit
+      int j = 0;
+      for (int32_t c0 = s0; c0 < s1; c0 += 256, ++j) {  // (at most kSteps steps: seg <= 256 * kSteps)
+        uint32_t kk[4];
+        keys4<true>(sh, x, c0 + 4 * lane, s1, kk);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const bool ok = c0 + 4 * lane + e < s1;
-          const uint32_t key = order_key(v[e]) & mask;
+          const uint32_t key = kk[e] & mask;
           lane_g += (ok && key > prefix) ? 1u : 0u;
-          eqb |= (ok && key == prefix ? 1u : 0u) << e;
+          eqb |= (ok && key == prefix ? 1u : 0u) << (4 * j + e);
         }
-        if (__ballot(eqb != 0u)) {  // wave-uniform
-          const uint32_t m = __builtin_popcount(eqb);
-          const uint32_t incl = wave_inclusive_scan_u32(m, lane);
-          uint32_t base = 0u;
-          if (lane == 63) base = atomicAdd(&sh.ncand, incl);
-          uint32_t at = __shfl(base, 63) + incl - m;
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if ((eqb >> e) & 1u) sh.cand[at++] = (uint32_t)(c0 + 4 * lane + e);
+      }
+      {
+        const uint32_t m = __builtin_popcount(eqb);
+        const uint32_t incl = wave_inclusive_scan_u32(m, lane);
+        uint32_t base = 0u;
+        if (lane == 63) base = atomicAdd(&sh.ncand, incl);
+        uint32_t at = __shfl(base, 63) + incl - m;
+        while (eqb != 0u) {
+          const int bit = __builtin_ctz(eqb);
+          sh.cand[at++] = (uint32_t)(s0 + 256 * (bit >> 2) + 4 * lane + (bit & 3));
+          eqb &= eqb - 1u;
         }
       }
       const uint32_t wg = __builtin_amdgcn_readlane(wave_inclusive_scan_u32(lane_g, lane), 63);
@@ -1410,7 +1444,7 @@ __device__ __forceinline__ void topk_row(TopkShared<THREADS, CAP, CAND>& sh, con
         const int shift = topk_shift(pass);
         const uint32_t dmask = topk_dmask(pass);
         for (int32_t i = tid; i < (int32_t)in_digit; i += THREADS) {
-          const uint32_t key = order_key(sh.vals[sh.cand[i]]);  // in_digit == the list's length
+          const uint32_t key = sh.vals[sh.cand[i]];  // in_digit == the list's length
           if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & dmask], 1u);
         }
       } else {
@@ -1425,7 +1459,7 @@ __device__ __forceinline__ void topk_row(TopkShared<THREADS, CAP, CAND>& sh, con
       // into the segment that holds them.
       for (int32_t i = tid; i < (int32_t)in_digit; i += THREADS) {
         const uint32_t pos = sh.cand[i];
-        const uint32_t key = order_key(sh.vals[pos]) & mask;
+        const uint32_t key = sh.vals[pos] & mask;
         const int w = (int)(pos / (uint32_t)seg);
         if (key > prefix) atomicAdd(&sh.wave_gt[w], 1u);
         else if (key == prefix) atomicAdd(&sh.wave_eq[w], 1u);
@@ -1440,14 +1474,14 @@ __device__ __forceinline__ void topk_row(TopkShared<THREADS, CAP, CAND>& sh, con
   // packed (keys above the threshold in the low 16 bits, keys at it in the
   // high 16; a step holds 256 positions), and one wave scan per step orders
   // them; running totals are 32-bit.
-  auto classify = [&](int32_t c0, float (&v)[4], uint32_t& bits) -> uint32_t {
-    row4<RES>(sh, x, c0 + 4 * lane, s1, v);
+  auto classify = [&](int32_t c0, uint32_t (&kk)[4], uint32_t& bits) -> uint32_t {
+    keys4<RES>(sh, x, c0 + 4 * lane, s1, kk);
     uint32_t c = 0u;
     bits = 0u;  // bit e: above, bit 4+e: at the threshold
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const bool ok = c0 + 4 * lane + e < s1;
-      const uint32_t key = order_key(v[e]) & mask;
+      const uint32_t key = kk[e] & mask;
       const uint32_t gt = (ok && key > prefix) ? 1u : 0u, eq = (ok && key == prefix) ? 1u : 0u;
       c += gt | (eq << 16);
       bits |= (gt << e) | (eq << (4 + e));
@@ -1457,9 +1491,8 @@ __device__ __forceinline__ void topk_row(TopkShared<THREADS, CAP, CAND>& sh, con
   if (!counted) {
     uint32_t lane_g = 0u, lane_q = 0u;
     for (int32_t c0 = s0; c0 < s1; c0 += 256) {
-      float v[4];
-      uint32_t bits;
-      const uint32_t c = classify(c0, v, bits);
+      uint32_t kk[4], bits;
+      const uint32_t c = classify(c0, kk, bits);
       lane_g += c & 0xFFFFu;
       lane_q += c >> 16;
     }
@@ -1477,9 +1510,8 @@ __device__ __forceinline__ void topk_row(TopkShared<THREADS, CAP, CAND>& sh, con
     q += sh.wave_eq[w];
   }
   for (int32_t c0 = s0; c0 < s1; c0 += 256) {
-    float v[4];
-    uint32_t bits;
-    const uint32_t c = classify(c0, v, bits);
+    uint32_t kk[4], bits;
+    const uint32_t c = classify(c0, kk, bits);
     const uint32_t incl = wave_inclusive_scan_u32(c, lane), ex = incl - c;
     uint32_t gl = g + (ex & 0xFFFFu), ql = q + (ex >> 16);  // before this lane's first position
 #pragma unroll
@@ -1488,7 +1520,7 @@ __device__ __forceinline__ void topk_row(TopkShared<THREADS, CAP, CAND>& sh, con
       const uint32_t slot = gl + min(ql, need);  // a key at the threshold: gl + ql when taken
       if (gt || (eq && ql < need)) {
         io[slot] = c0 + 4 * lane + e;
-        if (vo) vo[slot] = v[e];
+        if (vo) vo[slot] = key_value(kk[e], x, c0 + 4 * lane + e);
       }
       gl += gt ? 1u : 0u;
       ql += eq ? 1u : 0u;
@@ -1535,7 +1567,7 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(const float* logits, int6
                                            (lds_ptr)(&sh.vals[4 * THREADS * j + 256 * wave]), 16, 0, 0);
       }
       if (tid == 0)
-        for (int32_t i = L & ~3; i < L; ++i) sh.vals[i] = x[i];
+        for (int32_t i = L & ~3; i < L; ++i) sh.vals[i] = __float_as_uint(x[i]);
       __builtin_amdgcn_s_waitcnt(wait_vm(0));  // the DMAs are not covered by the compiler's waits
       __syncthreads();
       topk_row<true>(sh, x, L, k, io, vo);
