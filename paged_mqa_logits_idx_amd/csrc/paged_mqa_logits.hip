@@ -1203,10 +1203,10 @@ __global__ __launch_bounds__(64 * kStoreWaves) void store_keys_kernel(const uint
 // owns a contiguous segment of the row, 4 positions per lane and 256 per
 // step, counts its candidates per lane, and emits them after a prefix over
 // the waves' counts and one wave scan per step.
-// A row of at most CAP candidates is staged once in LDS (by DMA) and every
-// pass reads it there; the first pass replaces each value by its order key,
-// so later passes read keys, and a selected value is its key inverted (read
-// again from the row only for NaN and zeros).  After the first digit, one
+// A row of at most CAP candidates is read from memory once, by the first
+// pass, which stages each value's order key in LDS; later passes read the
+// keys there, and a selected value is its key inverted (read again from the
+// row only for NaN and zeros).  After the first digit, one
 // sweep over the waves' segments counts each segment's keys above that digit
 // and lists the positions of the keys in it (at most CAND of them).  The
 // later digits scan the list instead of the row, and the segments' counts
@@ -1217,7 +1217,7 @@ constexpr int kTopkBins = 2048;
 
 template <int THREADS, int CAP, int CAND>
 struct TopkShared {
-  uint32_t vals[CAP];    // the staged row: its values' bits, then (from the first pass on) their order keys
+  uint32_t vals[CAP];    // the staged row's order keys, when it fits
   uint32_t cand[CAND];   // positions of the keys sharing the first digit
   uint32_t hist[kTopkBins];
   uint32_t wave_gt[THREADS / 64], wave_eq[THREADS / 64];
@@ -1270,8 +1270,8 @@ __device__ __forceinline__ void load4(const float* x, int32_t i, int32_t L, floa
 }
 
 // Four consecutive order keys starting at i (a multiple of 4), 0 at or past
-// L.  RES: the staged row, which holds keys once the first pass has keyed it;
-// otherwise the values in memory, keyed here.
+// L.  RES: from the stage, which the first pass has filled; otherwise from the
+// values in memory, keyed here.
 template <bool RES, typename SH>
 __device__ __forceinline__ void keys4(const SH& sh, const float* x, int32_t i, int32_t L, uint32_t (&kk)[4]) {
   if constexpr (RES) {
@@ -1344,8 +1344,8 @@ __device__ __forceinline__ uint32_t radix_step(SH& sh, int pass, uint32_t& prefi
   return sh.pick[2];
 }
 
-// Histogram of one digit over the row's keys that match (prefix, mask).  The
-// first pass over a staged row replaces each value there by its order key.
+// Histogram of one digit over the row's keys that match (prefix, mask).  RES:
+// the first pass reads the row from memory and stages its keys.
 template <bool RES, int THREADS, int STEPS, typename SH>
 __device__ __forceinline__ void row_histogram(SH& sh, const float* x, int32_t L, int pass, uint32_t prefix,
                                               uint32_t mask) {
@@ -1353,28 +1353,43 @@ __device__ __forceinline__ void row_histogram(SH& sh, const float* x, int32_t L,
   const uint32_t dmask = topk_dmask(pass);
   auto count4 = [&](int32_t i) {
     uint32_t kk[4];
-    if (RES && pass == 0) {
-      if (i + 4 <= L) {
-        const u32x4 t = *reinterpret_cast<const u32x4*>(&sh.vals[i]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) kk[e] = order_key(__uint_as_float(t[e]));
-        *reinterpret_cast<u32x4*>(&sh.vals[i]) = (u32x4){kk[0], kk[1], kk[2], kk[3]};
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          kk[e] = (i + e < L) ? order_key(__uint_as_float(sh.vals[i + e])) : 0u;
-          if (i + e < L) sh.vals[i + e] = kk[e];
-        }
-      }
-    } else {
-      keys4<RES>(sh, x, i, L, kk);
-    }
+    keys4<RES>(sh, x, i, L, kk);
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       if (i + e < L && (kk[e] & mask) == prefix) atomicAdd(&sh.hist[(kk[e] >> shift) & dmask], 1u);
   };
   const int tid = threadIdx.x;
   if constexpr (RES) {
+    if (pass == 0) {
+      // The row comes from memory: every load is in flight before the first
+      // key is written to the stage and counted.
+      float v[STEPS][4];
+#pragma unroll
+      for (int j = 0; j < STEPS; ++j) {
+        const int32_t i = 4 * THREADS * j + 4 * tid;
+        if (i < L) load4(x, i, L, v[j]);
+      }
+#pragma unroll
+      for (int j = 0; j < STEPS; ++j) {
+        const int32_t i = 4 * THREADS * j + 4 * tid;
+        if (i < L) {
+          uint32_t kk[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) kk[e] = order_key(v[j][e]);
+          if (i + 4 <= L) {
+            *reinterpret_cast<u32x4*>(&sh.vals[i]) = (u32x4){kk[0], kk[1], kk[2], kk[3]};
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (i + e < L) sh.vals[i + e] = kk[e];
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (i + e < L) atomicAdd(&sh.hist[(kk[e] >> shift) & dmask], 1u);  // (pass 0 matches every key)
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < STEPS; ++j) {  // STEPS 16-byte groups per thread cover the staged row
       const int32_t i = 4 * THREADS * j + 4 * tid;
@@ -1555,21 +1570,7 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(const float* logits, int6
         if (vo) vo[t] = x[t];
       }
     } else if (L <= CAP) {
-      // Stage the row in LDS by DMA (16 bytes per lane, lane-linear within
-      // the wave's 1 KiB), all of it in flight at once; the last L % 4 values
-      // by thread 0.
-      const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-#pragma unroll
-      for (int j = 0; j < (CAP + 4 * THREADS - 1) / (4 * THREADS); ++j) {
-        const int32_t i = 4 * THREADS * j + 4 * tid;
-        if (i + 4 <= L)
-          __builtin_amdgcn_global_load_lds((global_ptr)(x + i),
-                                           (lds_ptr)(&sh.vals[4 * THREADS * j + 256 * wave]), 16, 0, 0);
-      }
-      if (tid == 0)
-        for (int32_t i = L & ~3; i < L; ++i) sh.vals[i] = __float_as_uint(x[i]);
-      __builtin_amdgcn_s_waitcnt(wait_vm(0));  // the DMAs are not covered by the compiler's waits
-      __syncthreads();
+      __syncthreads();  // (the histogram is clear; the first pass stages the row's keys)
       topk_row<true>(sh, x, L, k, io, vo);
     } else {
       __syncthreads();
