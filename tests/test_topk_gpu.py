@@ -100,6 +100,31 @@ def test_topk_reads_only_live_positions(lib):
     check_selection(lib, vals, seqlens, k, row_stride=3072)
 
 
+@pytest.mark.parametrize("ncols,list_cap", [(6144, 1024), (20000, 4096)])
+@pytest.mark.parametrize("extra", [-1, 0, 1])
+def test_topk_first_digit_at_list_capacity(lib, ncols, list_cap, extra):
+    """Rows whose first 11-bit digit (sign, exponent and two mantissa bits)
+    holds list_cap - 1, list_cap or list_cap + 1 keys: the kernel's candidate
+    list for that row size (256-thread rows up to 6144 wide, 1024-thread rows
+    above) is just filled or just overflows into the full-row passes.  Keys in
+    the digit are distinct values in [5, 5.5) plus repeats, so the later
+    digits and the tie rule both decide."""
+    rng = np.random.default_rng(ncols + extra)
+    rows, k = 3, 3000 if ncols > 6144 else 700
+    n_in = list_cap + extra
+    vals = np.full((rows, ncols), -1.0, dtype=np.float32)
+    for b in range(rows):
+        pos = rng.permutation(ncols)
+        high = k // 3                                           # a higher digit: all taken
+        digit = (5.0 + rng.integers(0, n_in // 3, size=n_in) * 1e-4).astype(np.float32)
+        assert np.all((digit.view(np.uint32) >> 21) == (np.float32(5.0).view(np.uint32) >> 21))
+        vals[b, pos[:high]] = 100.0
+        vals[b, pos[high:high + n_in]] = digit
+    seqlens = np.full(rows, ncols, dtype=np.int32)
+    seqlens[2] = ncols - 5
+    check_selection(lib, vals, seqlens, k)
+
+
 def fused(lib, wl, k, canary=7.0):
     announce(f"fused topk {wl.key_kind} rows={wl.rows} width={wl.table_width} k={k} "
              f"pt_stride={wl.pt_stride} ({wl.name})")
