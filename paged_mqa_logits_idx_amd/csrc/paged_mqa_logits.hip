@@ -1547,14 +1547,15 @@ __device__ __forceinline__ void topk_row(TopkShared<THREADS, CAP, CAND>& sh, con
   __syncthreads();  // wave_gt / wave_eq / vals / cand are rewritten by the next row
 }
 
-template <int THREADS, int CAP, int CAND>
+template <int THREADS, int CAP, int CAND, bool LAST_FIRST>
 __global__ __launch_bounds__(THREADS) void topk_kernel(const float* logits, int64_t row_stride,
                                                        const int32_t* seqlens, int32_t rows, int32_t ncols,
                                                        int32_t k, int32_t* idx_out, float* val_out) {
   __shared__ __attribute__((aligned(16))) TopkShared<THREADS, CAP, CAND> sh;
   const int tid = threadIdx.x;
   for (int i = tid; i < kTopkBins; i += THREADS) sh.hist[i] = 0u;  // wave 0 re-clears after each pick
-  for (int32_t b = blockIdx.x; b < rows; b += gridDim.x) {
+  for (int32_t rb = blockIdx.x; rb < rows; rb += gridDim.x) {
+    const int32_t b = LAST_FIRST ? rows - 1 - rb : rb;
     const int32_t L = min(max(seqlens[b], 0), ncols);
     const float* x = logits + (int64_t)b * row_stride;
     int32_t* io = idx_out + (int64_t)b * k;
@@ -1725,20 +1726,32 @@ int validate_topk(const float* logits, int64_t row_stride, const int32_t* seqlen
 }
 
 // Rows of at most 6144 candidates (ncols bounds every L) take 256-thread
-// workgroups staging up to 6144 values (four fit one CU's LDS); longer ones
-// 1024 threads staging up to 32768.
+// workgroups staging up to 6144 keys (four fit one CU's LDS); longer ones
+// 1024 threads staging up to 32768 (one per CU).  When there are more rows
+// than resident workgroups, rows wait for a free workgroup and are taken last
+// first: under a causal limit the later rows are the longer ones, and
+// starting them first leaves the short rows to fill the end of the launch.
 void launch_topk(const float* logits, int64_t row_stride, const int32_t* seqlens, int32_t rows,
                  int32_t ncols, int32_t k, int32_t* topk_idx, float* topk_val, hipStream_t stream) {
+  const int64_t cus = device_cu_count();
   if (ncols <= 6144) {
-    const int64_t cap = (int64_t)64 * device_cu_count();
-    const int64_t grid = rows < cap ? rows : cap;
-    topk_kernel<256, 6144, 1024><<<dim3((uint32_t)grid), dim3(256), 0, stream>>>(
-        logits, row_stride, seqlens, rows, ncols, k, topk_idx, topk_val);
+    const int64_t cap = 64 * cus;
+    const dim3 grid((uint32_t)(rows < cap ? rows : cap));
+    if (rows > 4 * cus)
+      topk_kernel<256, 6144, 1024, true><<<grid, dim3(256), 0, stream>>>(logits, row_stride, seqlens, rows,
+                                                                          ncols, k, topk_idx, topk_val);
+    else
+      topk_kernel<256, 6144, 1024, false><<<grid, dim3(256), 0, stream>>>(logits, row_stride, seqlens, rows,
+                                                                           ncols, k, topk_idx, topk_val);
   } else {
-    const int64_t cap = (int64_t)16 * device_cu_count();
-    const int64_t grid = rows < cap ? rows : cap;
-    topk_kernel<1024, 32768, 4096><<<dim3((uint32_t)grid), dim3(1024), 0, stream>>>(
-        logits, row_stride, seqlens, rows, ncols, k, topk_idx, topk_val);
+    const int64_t cap = 16 * cus;
+    const dim3 grid((uint32_t)(rows < cap ? rows : cap));
+    if (rows > cus)
+      topk_kernel<1024, 32768, 4096, true><<<grid, dim3(1024), 0, stream>>>(logits, row_stride, seqlens, rows,
+                                                                             ncols, k, topk_idx, topk_val);
+    else
+      topk_kernel<1024, 32768, 4096, false><<<grid, dim3(1024), 0, stream>>>(logits, row_stride, seqlens, rows,
+                                                                              ncols, k, topk_idx, topk_val);
   }
 }
 

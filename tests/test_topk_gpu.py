@@ -81,7 +81,9 @@ def check_selection(lib, vals, seqlens, k, row_stride=None):
     (9, 12288, 4096, "ties"), (9, 70000, 3, "normal"),
     (5, 30000, 2048, "equal"),   # first digit holds more keys than the candidate list
     (5, 6144, 700, "equal"), (6, 20000, 2048, "sample_low"), (6, 20000, 2048, "sample_high"),
-    (6, 5000, 2048, "sample_low"), (6, 5000, 300, "sample_high")])
+    (6, 5000, 2048, "sample_low"), (6, 5000, 300, "sample_high"),
+    (300, 6200, 64, "normal"),   # more rows than one-per-CU workgroups: taken last first
+    (1100, 700, 200, "ties")])   # more rows than four-per-CU workgroups: taken last first
 def test_topk_bit_exact(lib, rows, ncols, k, kind):
     rng = np.random.default_rng(rows * 7 + ncols + k)
     vals = values_of(rng, kind, rows, ncols)
