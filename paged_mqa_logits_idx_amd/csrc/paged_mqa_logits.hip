@@ -49,6 +49,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <type_traits>
 
 #include "paged_mqa_logits.h"
 
@@ -1223,6 +1224,7 @@ struct TopkShared {
   uint32_t wave_gt[THREADS / 64], wave_eq[THREADS / 64];
   uint32_t pick[3];      // chosen digit, candidates in the digits above it, in it
   uint32_t ncand;
+  uint32_t special;      // the staged row holds a NaN or a -0 (checked when values are returned)
 };
 
 // Unsigned order equals the value order; -0 and +0 share a key; NaN gets 0,
@@ -1292,9 +1294,11 @@ __device__ __forceinline__ void keys4(const SH& sh, const float* x, int32_t i, i
 
 // The value of position pos of row x, given its order key: the key inverted,
 // or for the two keys that lose bits (0: NaN, any payload; 0x80000000: +0 or
-// -0) the value itself, read from the row.
+// -0) the value itself, read from the row.  PLAIN: the row holds no NaN and
+// no -0, so every key inverts (0x80000000 to +0) and nothing is read.
+template <bool PLAIN>
 __device__ __forceinline__ float key_value(uint32_t key, const float* x, int32_t pos) {
-  if (key == 0u || key == 0x80000000u) return x[pos];
+  if (!PLAIN && (key == 0u || key == 0x80000000u)) return x[pos];
   return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
 }
 
@@ -1348,7 +1352,7 @@ __device__ __forceinline__ uint32_t radix_step(SH& sh, int pass, uint32_t& prefi
 // the first pass reads the row from memory and stages its keys.
 template <bool RES, int THREADS, int STEPS, typename SH>
 __device__ __forceinline__ void row_histogram(SH& sh, const float* x, int32_t L, int pass, uint32_t prefix,
-                                              uint32_t mask) {
+                                              uint32_t mask, bool find_special = false) {
   const int shift = topk_shift(pass);
   const uint32_t dmask = topk_dmask(pass);
   auto count4 = [&](int32_t i) {
@@ -1369,13 +1373,18 @@ __device__ __forceinline__ void row_histogram(SH& sh, const float* x, int32_t L,
         const int32_t i = 4 * THREADS * j + 4 * tid;
         if (i < L) load4(x, i, L, v[j]);
       }
+      bool special = false;  // a NaN or a -0 (whose keys do not invert to them)
 #pragma unroll
       for (int j = 0; j < STEPS; ++j) {
         const int32_t i = 4 * THREADS * j + 4 * tid;
         if (i < L) {
           uint32_t kk[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) kk[e] = order_key(v[j][e]);
+          for (int e = 0; e < 4; ++e) {
+            kk[e] = order_key(v[j][e]);
+            if (find_special)
+              special |= i + e < L && (v[j][e] != v[j][e] || __float_as_uint(v[j][e]) == 0x80000000u);
+          }
           if (i + 4 <= L) {
             *reinterpret_cast<u32x4*>(&sh.vals[i]) = (u32x4){kk[0], kk[1], kk[2], kk[3]};
           } else {
@@ -1388,6 +1397,7 @@ __device__ __forceinline__ void row_histogram(SH& sh, const float* x, int32_t L,
             if (i + e < L) atomicAdd(&sh.hist[(kk[e] >> shift) & dmask], 1u);  // (pass 0 matches every key)
         }
       }
+      if (special) sh.special = 1u;  // (read after the next barrier)
       return;
     }
 #pragma unroll
@@ -1413,7 +1423,7 @@ __device__ __forceinline__ void topk_row(TopkShared<THREADS, CAP, CAND>& sh, con
   const int32_t s0 = min(wave * seg, L), s1 = min(s0 + seg, L);
   // Radix select.  Invariant: 1 <= need <= candidates matching (prefix, mask).
   uint32_t prefix = 0u, mask = 0u, need = (uint32_t)k;
-  row_histogram<RES, THREADS, kSteps>(sh, x, L, 0, prefix, mask);
+  row_histogram<RES, THREADS, kSteps>(sh, x, L, 0, prefix, mask, vo != nullptr);
   uint32_t in_digit = radix_step(sh, 0, prefix, mask, need, wave, lane);
   bool counted = false;  // sh.wave_gt / wave_eq hold the segments' counts
   if (need != in_digit) {
@@ -1524,26 +1534,33 @@ __device__ __forceinline__ void topk_row(TopkShared<THREADS, CAP, CAND>& sh, con
     g += sh.wave_gt[w];
     q += sh.wave_eq[w];
   }
-  for (int32_t c0 = s0; c0 < s1; c0 += 256) {
-    uint32_t kk[4], bits;
-    const uint32_t c = classify(c0, kk, bits);
-    const uint32_t incl = wave_inclusive_scan_u32(c, lane), ex = incl - c;
-    uint32_t gl = g + (ex & 0xFFFFu), ql = q + (ex >> 16);  // before this lane's first position
+  // A row with no NaN and no -0 takes a loop whose values are the inverted
+  // keys alone: a load there would make every value store wait for all the
+  // stores before it (the memory counter retires in order).
+  auto emit = [&](auto plain) {
+    for (int32_t c0 = s0; c0 < s1; c0 += 256) {
+      uint32_t kk[4], bits;
+      const uint32_t c = classify(c0, kk, bits);
+      const uint32_t incl = wave_inclusive_scan_u32(c, lane), ex = incl - c;
+      uint32_t gl = g + (ex & 0xFFFFu), ql = q + (ex >> 16);  // before this lane's first position
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const bool gt = (bits >> e) & 1u, eq = (bits >> (4 + e)) & 1u;
-      const uint32_t slot = gl + min(ql, need);  // a key at the threshold: gl + ql when taken
-      if (gt || (eq && ql < need)) {
-        io[slot] = c0 + 4 * lane + e;
-        if (vo) vo[slot] = key_value(kk[e], x, c0 + 4 * lane + e);
+      for (int e = 0; e < 4; ++e) {
+        const bool gt = (bits >> e) & 1u, eq = (bits >> (4 + e)) & 1u;
+        const uint32_t slot = gl + min(ql, need);  // a key at the threshold: gl + ql when taken
+        if (gt || (eq && ql < need)) {
+          io[slot] = c0 + 4 * lane + e;
+          if (vo) vo[slot] = key_value<decltype(plain)::value>(kk[e], x, c0 + 4 * lane + e);
+        }
+        gl += gt ? 1u : 0u;
+        ql += eq ? 1u : 0u;
       }
-      gl += gt ? 1u : 0u;
-      ql += eq ? 1u : 0u;
+      const uint32_t tot = __builtin_amdgcn_readlane(incl, 63);
+      g += tot & 0xFFFFu;
+      q += tot >> 16;
     }
-    const uint32_t tot = __builtin_amdgcn_readlane(incl, 63);
-    g += tot & 0xFFFFu;
-    q += tot >> 16;
-  }
+  };
+  if (RES && sh.special == 0u) emit(std::true_type{});
+  else emit(std::false_type{});
   __syncthreads();  // wave_gt / wave_eq / vals / cand are rewritten by the next row
 }
 
@@ -1564,7 +1581,10 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(const float* logits, int6
       io[t] = -1;
       if (vo) vo[t] = -INFINITY;
     }
-    if (tid == 0) sh.ncand = 0u;
+    if (tid == 0) {
+      sh.ncand = 0u;
+      sh.special = 0u;
+    }
     if (L <= k) {  // every candidate is selected
       for (int32_t t = tid; t < L; t += THREADS) {
         io[t] = t;
