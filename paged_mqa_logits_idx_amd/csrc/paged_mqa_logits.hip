@@ -1207,7 +1207,7 @@ __global__ __launch_bounds__(64 * kStoreWaves) void store_keys_kernel(const uint
 // A row of at most CAP candidates is read from memory once, by the first
 // pass, which stages each value's order key in LDS; later passes read the
 // keys there, and a selected value is its key inverted (read again from the
-// row only for NaN and zeros).  After the first digit, one
+// row for NaN and zeros only in a row that holds a NaN or a -0).  After the first digit, one
 // sweep over the waves' segments counts each segment's keys above that digit
 // and lists the positions of the keys in it (at most CAND of them).  The
 // later digits scan the list instead of the row, and the segments' counts
