@@ -39,6 +39,12 @@ def values_of(rng, kind, rows, ncols):
         v = np.full((rows, ncols), 1.5, dtype=np.float32)
         v[:, ::97] = 2.0
         return v
+    if kind == "zeros":
+        # +0 and -0 (equal values) among small numbers, no NaN: the selected
+        # zeros must come back with their own sign bits
+        v = np.round(rng.standard_normal((rows, ncols)) * 0.8).astype(np.float32)
+        v[v == 0] = np.where(rng.random(int((v == 0).sum())) < 0.5, np.float32(-0.0), np.float32(0.0))
+        return v
     if kind in ("sample_low", "sample_high"):
         # every 8th position far below / above the rest: a guess taken from
         # those positions alone misplaces the k-th value (or finds it there)
@@ -82,6 +88,7 @@ def check_selection(lib, vals, seqlens, k, row_stride=None):
     (5, 30000, 2048, "equal"),   # first digit holds more keys than the candidate list
     (5, 6144, 700, "equal"), (6, 20000, 2048, "sample_low"), (6, 20000, 2048, "sample_high"),
     (6, 5000, 2048, "sample_low"), (6, 5000, 300, "sample_high"),
+    (6, 3000, 2000, "zeros"), (6, 9000, 7000, "zeros"),
     (300, 6200, 64, "normal"),   # more rows than one-per-CU workgroups: taken last first
     (1100, 700, 200, "ties")])   # more rows than four-per-CU workgroups: taken last first
 def test_topk_bit_exact(lib, rows, ncols, k, kind):
