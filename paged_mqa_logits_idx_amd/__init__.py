@@ -119,6 +119,33 @@ def _addr(x) -> int | None:
     return int(x)
 
 
+def _check(name: str, x, dtype, dense_rows: bool = False) -> None:
+    """A tensor argument must have the element type the kernels read and the
+    dense layout they assume: contiguous, or (``dense_rows``: tables and logits,
+    whose row stride is passed separately) unit stride along its last dim.
+    Raw addresses are passed through unchecked."""
+    if not isinstance(x, torch.Tensor):
+        return
+    if x.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {x.dtype}")
+    ok = (x.dim() == 0 or x.stride(-1) == 1 or x.shape[-1] <= 1) if dense_rows else x.is_contiguous()
+    if not ok:
+        raise ValueError(f"{name} must be " + ("unit-stride along its last dim" if dense_rows
+                                                 else "contiguous"))
+
+
+def _check_logits_args(q, kv_pages, kscale, page_table, seqlens, weights, out):
+    _check("q", q, torch.bfloat16)
+    if isinstance(kv_pages, torch.Tensor) and not kv_pages.is_contiguous():
+        raise ValueError("kv_pages must be contiguous")
+    if isinstance(kscale, torch.Tensor):
+        _check("kscale", kscale, torch.float32)
+    _check("page_table", page_table, torch.int32, dense_rows=True)
+    _check("seqlens", seqlens, torch.int32)
+    _check("weights", weights, torch.float32)
+    _check("out", out, torch.float32)
+
+
 def _stream_handle(stream, device) -> int | None:
     if stream is None:
         return torch.cuda.current_stream(device).cuda_stream
@@ -130,6 +157,7 @@ def _stream_handle(stream, device) -> int | None:
 def _call(name, q, kv_pages, kscale, page_table, seqlens, weights, out, *, rows, num_heads,
           head_dim, table_width, num_pages, kv_page_stride, kscale_page_stride,
           page_table_row_stride, stream, check):
+    _check_logits_args(q, kv_pages, kscale, page_table, seqlens, weights, out)
     dev = q.device if isinstance(q, torch.Tensor) else None
     fn = getattr(_lib, name)
     status = fn(_addr(q), _addr(kv_pages), _addr(kscale), _addr(page_table), _addr(seqlens),
@@ -202,6 +230,8 @@ def _call_varlen(name, q, kv_pages, kscale, page_table, row_table, seqlens, weig
         rows = q.shape[0] if rows is None else rows
     num_heads = NUM_HEADS if num_heads is None else num_heads
     head_dim = HEAD_DIM if head_dim is None else head_dim
+    _check_logits_args(q, kv_pages, kscale, page_table, seqlens, weights, out)
+    _check("row_table", row_table, torch.int32)
     dev = q.device if isinstance(q, torch.Tensor) else None
     status = getattr(_lib, name)(
         _addr(q), _addr(kv_pages), _addr(kscale), _addr(page_table), _addr(row_table),
@@ -260,6 +290,10 @@ def idx_topk_logits(logits, seqlens, topk_idx, topk_val=None, *, k=None, rows=No
         row_stride = logits.stride(0) if row_stride is None else row_stride
     if k is None:
         k = topk_idx.shape[1]
+    _check("logits", logits, torch.float32, dense_rows=True)
+    _check("seqlens", seqlens, torch.int32)
+    _check("topk_idx", topk_idx, torch.int32)
+    _check("topk_val", topk_val, torch.float32)
     dev = topk_idx.device if isinstance(topk_idx, torch.Tensor) else None
     status = _lib.idx_topk_logits(_addr(logits), int(row_stride), _addr(seqlens), int(rows),
                                   int(ncols), int(k), _addr(topk_idx), _addr(topk_val),
@@ -276,6 +310,9 @@ def _call_topk(name, q, kv_pages, kscale, page_table, seqlens, weights, logits, 
         q, page_table, table_width, rows, num_heads, head_dim, page_table_row_stride)
     if k is None:
         k = topk_idx.shape[1]
+    _check_logits_args(q, kv_pages, kscale, page_table, seqlens, weights, logits)
+    _check("topk_idx", topk_idx, torch.int32)
+    _check("topk_val", topk_val, torch.float32)
     dev = q.device if isinstance(q, torch.Tensor) else None
     status = getattr(_lib, name)(
         _addr(q), _addr(kv_pages), _addr(kscale), _addr(page_table), _addr(seqlens),
@@ -325,6 +362,12 @@ def idx_store_keys_fp8(keys, slots, kv_pages, kscale, *, num_pages, n=None,
     """
     if n is None:
         n = keys.shape[0]
+    _check("keys", keys, torch.bfloat16)
+    _check("slots", slots, torch.int64)
+    if isinstance(kscale, torch.Tensor):
+        _check("kscale", kscale, torch.float32)
+    if isinstance(kv_pages, torch.Tensor) and not kv_pages.is_contiguous():
+        raise ValueError("kv_pages must be contiguous")
     dev = keys.device if isinstance(keys, torch.Tensor) else None
     status = _lib.idx_store_keys_fp8(_addr(keys), _addr(slots), int(n), _addr(kv_pages),
                                      _addr(kscale), int(num_pages), int(kv_page_stride),
@@ -339,6 +382,10 @@ def idx_store_keys_bf16(keys, slots, kv_pages, *, num_pages, n=None, kv_page_str
     """Copy bf16 keys [n, 128] into 16384-byte bf16 pages at the given slots."""
     if n is None:
         n = keys.shape[0]
+    _check("keys", keys, torch.bfloat16)
+    _check("slots", slots, torch.int64)
+    if isinstance(kv_pages, torch.Tensor) and not kv_pages.is_contiguous():
+        raise ValueError("kv_pages must be contiguous")
     dev = keys.device if isinstance(keys, torch.Tensor) else None
     status = _lib.idx_store_keys_bf16(_addr(keys), _addr(slots), int(n), _addr(kv_pages),
                                       int(num_pages), int(kv_page_stride), _stream_handle(stream, dev))

@@ -994,11 +994,12 @@ __global__ __launch_bounds__(64 * kSharedRows) __attribute__((amdgpu_waves_per_e
     // unit's group gi: the table of the block's row gi, if no earlier row of
     // the block has it), with only that table's rows scoring -- the other
     // waves still copy their part of each page and meet every barrier.
-    // Table indices are scalar loads, re-read where needed.
+    // Table indices are scalar loads, re-read where needed; p.rt is read only
+    // at row indices below p.rows (the last block may hold fewer than 4 rows).
     auto table_of = [&](int32_t br) -> int32_t { return load_uniform(p.rt, br); };
+    if (MULTI && rb * kSharedRows + gi >= p.rows) continue;
     const int32_t T = MULTI ? table_of(rb * kSharedRows + gi) : 0;
     if constexpr (MULTI) {
-      if (rb * kSharedRows + gi >= p.rows) continue;
       bool lead = true;
       for (int r = 0; r < gi; ++r) lead = lead && table_of(rb * kSharedRows + r) != T;
       if (!lead) continue;

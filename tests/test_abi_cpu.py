@@ -252,3 +252,24 @@ VF, VB = "idx_paged_mqa_logits_varlen_fp8", "idx_paged_mqa_logits_varlen_bf16"
 ])
 def test_varlen_host_validation(lib, name, kw, status):
     assert _varlen(lib, name, **kw) == status
+
+
+def test_binding_checks_tensor_layouts():
+    """The binding refuses tensors whose element type or layout differs from
+    what the kernels read, before any call into the library."""
+    import torch
+
+    import paged_mqa_logits_idx_amd as b
+
+    b._check("q", torch.zeros((2, 64, 128), dtype=torch.bfloat16), torch.bfloat16)
+    with pytest.raises(ValueError, match="q must be torch.bfloat16"):
+        b._check("q", torch.zeros((2, 64, 128), dtype=torch.float32), torch.bfloat16)
+    with pytest.raises(ValueError, match="contiguous"):
+        b._check("weights", torch.zeros((64, 2)).t(), torch.float32)
+    with pytest.raises(ValueError, match="topk_idx must be torch.int32"):
+        b._check("topk_idx", torch.zeros((2, 8), dtype=torch.int64), torch.int32)
+    # tables and logits carry their own row stride: only the last dim must be dense
+    b._check("logits", torch.zeros((4, 100))[:, :64], torch.float32, dense_rows=True)
+    with pytest.raises(ValueError, match="unit-stride"):
+        b._check("logits", torch.zeros((100, 4)).t(), torch.float32, dense_rows=True)
+    b._check("kscale", 12345, torch.float32)  # raw addresses pass through

@@ -46,7 +46,7 @@ def check_full(lib, wl, label=""):
 # ---------------------------------------------------------------------------
 # the specified configurations
 
-@pytest.mark.parametrize("cfg", [0, 1, 2])
+@pytest.mark.parametrize("cfg", [0, 1, 2, "2b"])
 def test_config_full(lib, cfg):
     st = check_full(lib, W.config(cfg))
     announce(f"config {cfg}: {st}")
@@ -60,17 +60,20 @@ def _sample_rows(wl, n, seed):
     return sorted(pick)
 
 
-@pytest.mark.parametrize("cfg", [3, "3c", 4])
+@pytest.mark.parametrize("cfg", [3, "3c", 4, "4f"])
 def test_config_sampled_rows(lib, cfg):
     """Full-size configurations in the benchmark's launch shape: every output's
-    mask checked; sampled rows checked against the oracle element by element."""
+    mask checked; sampled rows checked against the oracle element by element.
+    The 4096-row prefills (bf16 and fp8 keys) run whole-table units of 88
+    pages, so each wave's 24-page logits buffer is written out mid-unit."""
     wl = W.config(cfg)
     got = run(lib, wl)
     m = mask_of(wl)
     assert np.array_equal(np.isneginf(got), m)
     assert np.isfinite(got[~m]).all()
-    rows = _sample_rows(wl, 6 if cfg != 4 else 40, seed=5)
-    if cfg == 4:  # rows on both sides of 4-row block edges
+    prefill = cfg in (4, "4f")
+    rows = _sample_rows(wl, 40 if prefill else 6, seed=5)
+    if prefill:  # rows on both sides of 4-row block edges
         rows = sorted(set(rows) | {1, 2, 3, 4, 5, 2047, 2048, 4092, 4093, 4094})
     ref = oracle.paged_mqa_logits(wl, rows=rows)
     st = assert_parity(got[rows], ref, m[rows], label=str(cfg))
@@ -126,6 +129,25 @@ def test_prefill_shape_fp8_keys(lib):
     wl = W.random_workload(51, "fp8", rows=T, table_width=width, num_pages=width,
                            shared_table=True, seqlens=seq)
     check_full(lib, wl)
+
+
+@pytest.mark.parametrize("kind", ["fp8", "bf16"])
+def test_prefill_units_past_logits_buffer(lib, kind):
+    """Shared-table units longer than a wave's 24-page logits buffer, checked
+    in full: 4096 rows (1024 row blocks, so every unit is the whole 40-page
+    table), most rows short and every 97th row block long (28..40 pages), so
+    the buffer is written out in the middle of a unit and again at its end."""
+    rows, width = 4096, 40
+    rng = np.random.default_rng(98)
+    seq = rng.integers(1, 2 * P + 1, size=rows)
+    for rb in range(0, rows // 4, 97):
+        seq[4 * rb: 4 * rb + 4] = rng.integers(27 * P + 1, width * P + 1, size=4)
+    seq[-1] = width * P
+    wl = W.random_workload(98, kind, rows=rows, table_width=width, num_pages=width + 9,
+                           seqlens=seq, shared_table=True)
+    assert int(wl.lengths().max()) > 24 * P
+    st = check_full(lib, wl, label=f"prefill units > buffer {kind}")
+    announce(f"prefill units past the logits buffer {kind}: {st}")
 
 
 def test_decode_shape_bf16_keys(lib):

@@ -58,7 +58,7 @@ def expected_pool(pool0, codes, scales, slots, num_pages, kv_stride, ks_pool=Non
 
 def store_fp8(lib, bits, slots, num_pages, pool0, kv_stride=FUSED, ks0=None, ks_stride=FUSED,
               ks_offset=P * D):
-    keys = torch.from_numpy(bits.view(np.int16).copy()).cuda()
+    keys = torch.from_numpy(bits.view(np.int16).copy()).cuda().view(torch.bfloat16)
     sl = torch.from_numpy(np.asarray(slots, dtype=np.int64)).cuda()
     pool = torch.from_numpy(pool0.copy()).cuda()
     if ks0 is None:
@@ -144,7 +144,7 @@ def test_store_bf16_copies(lib):
     slots[::50] = -1
     stride = P * D * 2
     pool0 = rng.integers(0, 256, size=num_pages * stride, dtype=np.uint8)
-    keys = torch.from_numpy(bits.view(np.int16).copy()).cuda()
+    keys = torch.from_numpy(bits.view(np.int16).copy()).cuda().view(torch.bfloat16)
     pool = torch.from_numpy(pool0.copy()).cuda()
     lib.idx_store_keys_bf16(keys, torch.from_numpy(slots).cuda(), pool, num_pages=num_pages)
     torch.cuda.synchronize()
