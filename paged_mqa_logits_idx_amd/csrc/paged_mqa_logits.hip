@@ -42,8 +42,17 @@
 //   B (keys)   col  i = 16*nb + n,  8 k-values (same k-set as A for lane l),
 //   D          D[4*g + r][n] in accumulator element r.
 // The contraction is invariant under any permutation of k applied to both
-// operands, so lane group g takes the contiguous k-range [32g, 32g+32) and
-// MFMA kb in 0..3 takes its 8-value slice 32g + 8kb .. +8.
+// operands.  MFMA kb in 0..3 gives lane group g the 8 k-values
+//   k(kb, g) = 64*(kb/2) + 16*g + 8*(kb%2) .. +8,
+// so that
+//   * a query load (one kb, 16 bytes per lane) touches one 128-byte line per
+//     head row: the four lane groups read 16 bytes at 32-byte steps inside
+//     the same 128 bytes (16 lines per instruction, not the 32 of a layout
+//     with each lane group's k-range 64 bytes away from the next);
+//   * a lane's fp8 key bytes of one position are two 16-byte chunks, g and
+//     4 + g of the 128-byte row: chunk g holds kb = 0, 1 and chunk 4 + g
+//     kb = 2, 3 (bf16 keys: 16-byte chunks 2g, 2g+1, 8+2g, 9+2g of the
+//     256-byte row for kb = 0..3).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -117,9 +126,11 @@ __device__ __forceinline__ void load_row_query(const Params& p, int32_t b, int l
   const uint8_t* qrow = p.q + (int64_t)b * (kHeads * kDim * 2);
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(qrow + ((16 * mb + n) * kDim + 32 * g) * 2);
+    // k(kb, g) = 64*(kb/2) + 16*g + 8*(kb%2): byte offset 128*(kb/2) + 32*g + 16*(kb%2)
+    const uint8_t* hrow = qrow + (16 * mb + n) * (kDim * 2) + 32 * g;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) rq.a[mb][kb] = __builtin_bit_cast(bf16x8, src[kb]);
+    for (int kb = 0; kb < 4; ++kb)
+      rq.a[mb][kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(hrow + 128 * (kb >> 1) + 16 * (kb & 1)));
     rq.w[mb] = *reinterpret_cast<const f32x4*>(p.w + (int64_t)b * kHeads + 16 * mb + 4 * g);
   }
 }
@@ -130,12 +141,15 @@ __device__ __forceinline__ void load_page_global(const Params& p, int32_t gp, in
   const int n = lane & 15, g = lane >> 4;
   const uint8_t* base = p.kv + (int64_t)gp * p.kv_stride;
   constexpr int kRowBytes = (KEY == kFp8) ? kDim : 2 * kDim;
-  constexpr int kSlice = (KEY == kFp8) ? 32 : 64;  // bytes of 32 k-values
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(base + (16 * nb + n) * kRowBytes + kSlice * g);
+    const uint8_t* row = base + (16 * nb + n) * kRowBytes;
 #pragma unroll
-    for (int v = 0; v < PageKeys<KEY>::kVec; ++v) pk.v[nb][v] = __builtin_nontemporal_load(src + v);
+    for (int v = 0; v < PageKeys<KEY>::kVec; ++v) {
+      // fp8: 16-byte chunks g and 4 + g; bf16: chunks 2g, 2g+1, 8+2g, 9+2g
+      const int c = (KEY == kFp8) ? g + 4 * v : 8 * (v >> 1) + 2 * g + (v & 1);
+      pk.v[nb][v] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + 16 * c));
+    }
   }
   if constexpr (KEY == kFp8)
     pk.s = reinterpret_cast<const float*>(p.ks + (int64_t)gp * p.ks_stride)[lane];
@@ -419,7 +433,7 @@ __device__ __forceinline__ int32_t wave_inclusive_scan(int32_t v, int lane) {
 // chunk position l%8), so every instruction reads whole 128-byte lines.  The
 // slot keeps the rows in order but XOR-swizzles the chunks inside a row:
 // position c of row i holds key chunk c ^ (i % 8).  A B fragment then reads row
-// i = 16 nb + n, chunks 2g and 2g+1, at positions (2g+h) ^ (n % 8): the eight
+// i = 16 nb + n, chunks g and 4+g, at positions (g+4h) ^ (n % 8): the eight
 // lanes n = 0..7 of a lane group hit distinct banks.  The scales land at
 // slot + 8192 (lane l: scale of position l).  Per page: wait for the page's
 // DMA group, copy the slot into registers, refill the slot with the page two
@@ -450,10 +464,10 @@ __device__ __forceinline__ void dma_page(const uint8_t* keys, const uint8_t* sca
 }
 
 // Lane's LDS byte offsets (within a slot) of its two 16-byte B chunks of
-// position block 0; block nb adds 2048 nb.
+// position block 0 (chunks g and 4 + g of row n); block nb adds 2048 nb.
 __device__ __forceinline__ uint32_t slot_chunk_offset(int lane, int h) {
   const int n = lane & 15, g = lane >> 4;
-  return (uint32_t)(n * kDim + 16 * ((2 * g + h) ^ (n & 7)));
+  return (uint32_t)(n * kDim + 16 * ((g + 4 * h) ^ (n & 7)));
 }
 
 // Wait until at most N vector-memory operations are outstanding (the page's
@@ -576,7 +590,7 @@ __device__ __forceinline__ void fill_rest(const Params& p, FillCursor& fc, int l
 
 // bf16 page from its LDS slot into the lane's B fragments (rows of 256 B,
 // 16-byte chunk c of row i at chunk c ^ (i % 16)): lane (g, n) reads chunks
-// 4g .. 4g+3 of rows n, 16+n, 32+n, 48+n.  Waits
+// 2g, 2g+1, 8+2g, 9+2g of rows n, 16+n, 32+n, 48+n.  Waits
 // until at most N vector-memory operations are outstanding first (the
 // compiler does not see these reads, so it adds no wait for the DMAs still in
 // flight into other slots).
@@ -585,7 +599,7 @@ __device__ __forceinline__ void read_slot_bf16(uint32_t sb, int lane, PageKeys<k
   const int n = lane & 15, g = lane >> 4;
   uint32_t a[4];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) a[v] = sb + (uint32_t)(n * 256 + 16 * ((4 * g + v) ^ n));
+  for (int v = 0; v < 4; ++v) a[v] = sb + (uint32_t)(n * 256 + 16 * ((8 * (v >> 1) + 2 * g + (v & 1)) ^ n));
   asm volatile(
       "s_waitcnt vmcnt(%20)\n\t"
       "ds_read_b128 %0, %16\n\t"
@@ -914,7 +928,8 @@ __device__ __forceinline__ void read_shared_slot(uint32_t sb, int lane, PageKeys
     for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
       for (int v = 0; v < 4; ++v)
-        pk.v[nb][v] = *(lds_u32x4c*)(size_t)(sb + (uint32_t)(n * 256 + 16 * ((4 * g + v) ^ n)) + 4096 * nb);
+        pk.v[nb][v] = *(lds_u32x4c*)(size_t)(sb + (uint32_t)(n * 256 + 16 * ((8 * (v >> 1) + 2 * g + (v & 1)) ^ n)) +
+                                             4096 * nb);
     pk.s = 1.0f;
   } else {
     const uint32_t a0 = sb + slot_chunk_offset(lane, 0), a1 = sb + slot_chunk_offset(lane, 1);
