@@ -11,15 +11,17 @@ Prints ONE JSON line:
   roofline       HBM roofline of the kernel: algorithmic bytes per launch / mean
                  launch time (HIP events on the launch stream) vs 8 TB/s, with the
                  measured HBM traffic (rocprofv3 counters) and reachable
-                 denominators measured in the same run (a 1 GiB device copy, a
+                 denominators measured in the same run (the bare key-page read
+                 stream of libidx_read_stream.so, a torch 1 GiB device copy, a
                  bf16 8192^3 matrix product)
   cpu_baseline   the CPU oracle timed on a bounded row sample of the same workload
   secondary      same measurements for the 128-page decode, the 513-slot control
                  of the default workload, the bf16 prefill (MFMA roofline), the
                  crossed variants (bf16-key decode, fp8-key prefill), a
                  multi-request prefill (four requests, 4096 rows), the fused
-                 logits + top-2048 call (with the top-k kernel alone) on the
-                 default workload and the prefill, and the fp8 key store
+                 logits + top-2048 call (with the top-k kernel alone and its
+                 HBM roofline) on the default workload and the prefill, and the
+                 fp8 key store; each warmed until its replay time is steady
 
 Inputs are synthetic and seeded (workloads.py).  Key pools and outputs are
 rotated over enough copies that one launch's bytes are gone from the 256 MB
@@ -47,6 +49,11 @@ KERNEL_SOURCE = ROOT / "paged_mqa_logits_idx_amd" / "csrc" / "paged_mqa_logits.h
 TRAFFIC_FILE = ROOT / "profiles" / "traffic.json"
 ROTATE_BYTES = 1 << 30           # >= 4x the 256 MB last-level cache
 TOPK = 2048                      # indices kept per row by the fused top-k line
+SETTLE_GROUP_MS = 20.0           # secondary lines: untimed replay groups of >= 20 ms ...
+SETTLE_TOL = 0.02                # ... until two consecutive groups agree within 2%
+SETTLE_MAX_S = 3.0
+STREAM_LIB = ROOT / "paged_mqa_logits_idx_amd" / "libidx_read_stream.so"
+STREAM_POOL_PAGES = 131072       # 1.1 GB of 8448-byte pages for the read-stream denominator
 
 
 def log(msg: str) -> None:
@@ -91,11 +98,12 @@ def algorithmic_work(wl):
     return reads, writes, flops
 
 
-def measure(cfg, steps: int, warmup: int, topk: int | None = None):
+def measure(cfg, steps: int, warmup: int, topk: int | None = None, settle: bool = False):
     """Time `steps` back-to-back library calls on one GPU.
 
     With `topk`, the call is the fused logits + top-k entry point (k = topk),
     and the top-k kernel alone is timed as well over the logits it left.
+    settle: warm the captured graph until its replay time is steady (time_graph).
     """
     import torch
 
@@ -130,20 +138,21 @@ def measure(cfg, steps: int, warmup: int, topk: int | None = None):
 
         def step(i):
             W.run_library_topk(sets[i % n_sets], lib, idx[i % n_sets])
-    region_ms, wall = time_graph(step, steps, warmup)
+    region_ms, wall, replays = time_graph(step, steps, warmup, settle)
     mean_ms = region_ms / steps
     topk_ms = None
     if topk is not None:
         def topk_step(i):
             d = sets[i % n_sets]
             lib.idx_topk_logits(d.out, d.seqlens, idx[i % n_sets])
-        topk_ms = time_graph(topk_step, steps, warmup)[0] / steps
+        topk_ms = time_graph(topk_step, steps, warmup, settle)[0] / steps
     reads, writes, flops = algorithmic_work(wl)
     res = {
         "cfg": cfg, "name": wl.name, "rows": wl.rows, "table_width": wl.table_width,
         "key_kind": wl.key_kind, "live_positions": wl.live_positions(),
         "live_pages": wl.live_pages(), "sets": n_sets,
         "kernel_ms_mean": mean_ms, "region_ms": region_ms, "wall_s": wall, "steps": steps,
+        "untimed_replays": replays,
         "alg_read_bytes": reads, "alg_write_bytes": writes, "alg_flops": flops,
         "gbs": (reads + writes) / (mean_ms * 1e-3) / 1e9,
         "tflops": flops / (mean_ms * 1e-3) / 1e12,
@@ -155,10 +164,17 @@ def measure(cfg, steps: int, warmup: int, topk: int | None = None):
     return wl, res
 
 
-def time_graph(step, steps: int, warmup: int):
+def time_graph(step, steps: int, warmup: int, settle: bool = False):
     """Warm up on a side stream, capture `steps` calls of step(i) in one HIP
     graph (launches run back to back, no host submission gaps) and time one
-    replay with HIP events on the stream it runs on.  Returns (ms, wall s)."""
+    replay with HIP events on the stream it runs on.  Returns (ms, wall s,
+    untimed replays).
+
+    settle: before the timed replay, replay the graph untimed in groups of at
+    least SETTLE_GROUP_MS of GPU time until two consecutive groups agree
+    within SETTLE_TOL (at most SETTLE_MAX_S): the per-launch time of a line
+    measured right after other work, or after the GPU sat idle while inputs
+    were generated, drifts for tens of milliseconds, whatever --warmup is."""
     import torch
 
     side = torch.cuda.Stream()
@@ -172,19 +188,35 @@ def time_graph(step, steps: int, warmup: int):
     with torch.cuda.graph(graph):
         for i in range(steps):
             step(i)
-    graph.replay()  # untimed: first replay of the captured steps
-    torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def replay_ms(n: int) -> float:
+        a.record(stream)
+        for _ in range(n):
+            graph.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    first = replay_ms(1)  # untimed: first replay of the captured steps
+    replays = 1
+    if settle:
+        group = max(1, math.ceil(SETTLE_GROUP_MS / max(first, 1e-3)))
+        t_end = time.perf_counter() + SETTLE_MAX_S
+        prev = replay_ms(group)
+        replays += group
+        while time.perf_counter() < t_end:
+            cur = replay_ms(group)
+            replays += group
+            if abs(cur - prev) <= SETTLE_TOL * prev:
+                break
+            prev = cur
     w0 = time.perf_counter()
-    a.record(stream)
-    graph.replay()
-    b.record(stream)
-    torch.cuda.synchronize()
+    ms = replay_ms(1)
     wall = time.perf_counter() - w0
-    ms = a.elapsed_time(b)
     del graph
-    return ms, wall
+    return ms, wall, replays
 
 
 def achievable_peaks():
@@ -219,7 +251,51 @@ def achievable_peaks():
     return round(copy_gbs, 1), round(mm_tflops, 1)
 
 
-def measure_store(steps: int, warmup: int):
+def read_stream_rates(same_pages: int):
+    """Reachable HBM read rate of the decode's access pattern, measured here:
+    the bare key-page read stream of libidx_read_stream.so (random 8448-byte
+    pages into LDS by DMA, nt policy, the decode's grid; nothing computed or
+    stored).  Returns the rate over the whole 1.1 GB pool per launch, the
+    marginal rate between that and `same_pages` pages, and the time for
+    `same_pages` pages (launches rotate over disjoint page sets, >= 1 GB
+    apart, so no launch finds its pages in the last-level cache)."""
+    import ctypes
+
+    import torch
+
+    lib = ctypes.CDLL(str(STREAM_LIB))
+    lib.idx_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                    ctypes.c_int32, ctypes.c_void_p]
+    lib.idx_read_stream.restype = ctypes.c_int
+    lib.idx_read_stream_workgroups.restype = ctypes.c_int
+    page = 8448
+    pool = torch.ones(STREAM_POOL_PAGES * page, dtype=torch.uint8, device="cuda")
+    gen = torch.Generator().manual_seed(7)
+    ids = torch.randperm(STREAM_POOL_PAGES, generator=gen).to(torch.int32).cuda()
+    sink = torch.empty(4 * lib.idx_read_stream_workgroups(), dtype=torch.int32, device="cuda")
+
+    def timed(n: int) -> float:
+        sets = max(1, STREAM_POOL_PAGES // n)
+
+        def step(i):
+            rc = lib.idx_read_stream(pool.data_ptr(), ids.data_ptr() + 4 * n * (i % sets), n,
+                                     sink.data_ptr(), 0, torch.cuda.current_stream().cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"idx_read_stream failed ({rc})")
+        return time_graph(step, 20, 5, settle=True)[0] / 20
+
+    t_all = timed(STREAM_POOL_PAGES)
+    n = max(1, min(int(same_pages), STREAM_POOL_PAGES // 2))
+    t_same = timed(n)
+    b_all, b_same = STREAM_POOL_PAGES * page, n * page
+    del pool, ids, sink
+    torch.cuda.empty_cache()
+    return {"dma_read_stream_gbs": round(b_all / (t_all * 1e-3) / 1e9, 1),
+            "dma_read_stream_marginal_gbs": round((b_all - b_same) / ((t_all - t_same) * 1e-3) / 1e9, 1),
+            "dma_read_same_pages": n, "dma_read_same_pages_us": round(t_same * 1e3, 2)}
+
+
+def measure_store(steps: int, warmup: int, settle: bool = False):
     """fp8 key store: every slot of the 32,768-page pool (2,097,152 keys) per step.
 
     Keys arrive the way a prefill writes them: page after page of a request,
@@ -244,7 +320,7 @@ def measure_store(steps: int, warmup: int):
         lib.idx_store_keys_fp8(keys, slots, pool, pool.data_ptr() + W.FP8_KEY_BYTES,
                                num_pages=num_pages)
 
-    ms = time_graph(step, steps, warmup)[0] / steps
+    ms = time_graph(step, steps, warmup, settle)[0] / steps
     per_key = W.HEAD_DIM * 2 + 8 + W.HEAD_DIM + 4  # bf16 key + slot id in, codes + scale out
     alg = n * per_key
     del pools, keys, slots
@@ -361,18 +437,25 @@ def main() -> int:
     wl, main_res = measure(cfg, args.steps, args.warmup)
     log(json.dumps(main_res))
     copy_gbs, mm_tflops = achievable_peaks()
-    log(f"achievable: device copy {copy_gbs} GB/s, bf16 8192^3 matmul {mm_tflops} TFLOP/s")
+    stream = read_stream_rates(main_res["live_pages"])
+    stream_gbs = stream["dma_read_stream_gbs"]
+    log(f"achievable: key-page read stream {json.dumps(stream)}, torch device copy {copy_gbs} GB/s, "
+        f"bf16 8192^3 matmul {mm_tflops} TFLOP/s")
 
+    # Secondary lines: at least 20 timed launches, and each warmed until its
+    # replay time is steady (time_graph's settle), whatever --warmup is.
+    sec_steps, sec_warm = max(20, args.steps // 2), max(3, args.warmup // 2)
     secondary = {}
     if not args.no_secondary:
         for c in (2, "3c", 4, "2b", "4f", "varlen"):
             if str(c) == str(cfg):
                 continue
-            _, r = measure(c, max(10, args.steps // 2), max(3, args.warmup // 2))
+            _, r = measure(c, sec_steps, sec_warm, settle=True)
             log(json.dumps(r))
             entry = {
                 "workload": r["name"], "kernel_ms_mean": round(r["kernel_ms_mean"], 5),
-                "positions_per_s": r["positions_per_s_kernel"],
+                "positions_per_s": r["positions_per_s_kernel"], "steps": sec_steps,
+                "untimed_replays": r["untimed_replays"],
             }
             if r["shared_table"] or c == "varlen":  # prefill: one key read serves many rows
                 entry.update(bound="mfma", achieved_tflops=round(r["tflops"], 2),
@@ -383,20 +466,30 @@ def main() -> int:
             else:
                 entry.update(bound="hbm", achieved_gbs=round(r["gbs"], 1), peak_gbs=HBM_PEAK_GBS,
                              frac=round(r["gbs"] / HBM_PEAK_GBS, 4),
-                             frac_of_copy=round(r["gbs"] / copy_gbs, 4),
+                             frac_of_stream=round(r["gbs"] / stream_gbs, 4),
                              alg_bytes=r["alg_read_bytes"] + r["alg_write_bytes"])
+            entry["traffic"] = traffic_for(str(c), 0)
             secondary[str(c)] = entry
         for c in (cfg, 4):
-            _, r = measure(c, max(10, args.steps // 2), max(3, args.warmup // 2), topk=TOPK)
+            twl, r = measure(c, sec_steps, sec_warm, topk=TOPK, settle=True)
             log(json.dumps(r))
+            # top-k kernel alone: reads each row's live logits, writes k indices per row
+            tk_bytes = 4 * twl.live_positions() + 4 * TOPK * twl.rows
+            tk_gbs = tk_bytes / (r["topk_only_ms"] * 1e-3) / 1e9
             secondary[f"topk_{c}"] = {
                 "workload": f"{r['name']}, logits + top-{TOPK} (fused call, no -inf tail)",
                 "k": TOPK, "kernel_ms_mean": round(r["kernel_ms_mean"], 5),
                 "topk_only_ms": round(r["topk_only_ms"], 5),
-                "positions_per_s": r["positions_per_s_kernel"],
+                "positions_per_s": r["positions_per_s_kernel"], "steps": sec_steps,
+                "untimed_replays": r["untimed_replays"],
+                "topk_roofline": {"bound": "hbm", "achieved": round(tk_gbs, 1), "peak": HBM_PEAK_GBS,
+                                  "unit": "GB/s", "frac": round(tk_gbs / HBM_PEAK_GBS, 4),
+                                  "alg_bytes": tk_bytes, "traffic": traffic_for(f"topk_{c}", 0)},
             }
-        r = measure_store(max(10, args.steps // 2), max(3, args.warmup // 2))
-        r["frac_of_copy"] = round(r["achieved_gbs"] / copy_gbs, 4)
+        r = measure_store(sec_steps, sec_warm, settle=True)
+        r["frac_of_stream"] = round(r["achieved_gbs"] / stream_gbs, 4)
+        r["steps"] = sec_steps
+        r["traffic"] = traffic_for("store_fp8", 0)
         log(json.dumps(r))
         secondary["store_fp8"] = r
 
@@ -425,8 +518,8 @@ def main() -> int:
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                     "alg_bytes_per_launch": alg_bytes,
                     "kernel_ms_mean": round(main_res["kernel_ms_mean"], 5),
-                    "achievable": {"device_copy_gbs": copy_gbs,
-                                   "frac_of_copy": round(achieved / copy_gbs, 4),
+                    "achievable": {**stream, "frac_of_stream": round(achieved / stream_gbs, 4),
+                                   "torch_device_copy_gbs": copy_gbs,
                                    "bf16_matmul_tflops": mm_tflops}}
     out = {
         "metric": "indexer c4-positions scored/sec + achieved HBM GB/s (decode) / MFMA % (prefill)",

@@ -1,4 +1,6 @@
-"""Build step for the HIP library libidx_paged_mqa.so (gfx950, in-tree)."""
+"""Build step for the HIP libraries (gfx950, in-tree): libidx_paged_mqa.so, the
+indexer, and libidx_read_stream.so, the bare key-page read stream that the
+benchmark measures as the reachable HBM read rate."""
 from __future__ import annotations
 
 import os
@@ -10,6 +12,8 @@ PKG_DIR = Path(__file__).resolve().parent
 REPO_DIR = PKG_DIR.parent
 SOURCES = [PKG_DIR / "csrc" / "paged_mqa_logits.hip"]
 LIB_PATH = PKG_DIR / "libidx_paged_mqa.so"
+STREAM_SOURCES = [PKG_DIR / "csrc" / "read_stream.hip"]
+STREAM_LIB_PATH = PKG_DIR / "libidx_read_stream.so"
 ARCH = "gfx950"
 
 
@@ -20,7 +24,7 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP library cannot be built")
 
 
-def build_command(out: Path = LIB_PATH) -> list[str]:
+def build_command(out: Path = LIB_PATH, sources=None) -> list[str]:
     return [
         hipcc(),
         f"--offload-arch={ARCH}",
@@ -31,15 +35,20 @@ def build_command(out: Path = LIB_PATH) -> list[str]:
         # packed fp32 VALU ops are kept out of every kernel
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         f"-I{REPO_DIR / 'include'}",
-        *[str(s) for s in SOURCES],
+        *[str(s) for s in (SOURCES if sources is None else sources)],
         "-o", str(out),
     ]
 
 
 def build(verbose: bool = False) -> Path:
-    """Compile the library; always recompiles.  Writes atomically."""
-    tmp = LIB_PATH.with_name(LIB_PATH.name + ".tmp")
-    cmd = build_command(tmp)
+    """Compile both libraries; always recompiles.  Writes atomically."""
+    _compile(STREAM_LIB_PATH, STREAM_SOURCES, verbose)
+    return _compile(LIB_PATH, SOURCES, verbose)
+
+
+def _compile(lib: Path, sources, verbose: bool) -> Path:
+    tmp = lib.with_name(lib.name + ".tmp")
+    cmd = build_command(tmp, sources)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if verbose or res.returncode != 0:
         out = (res.stdout + res.stderr).strip()
@@ -49,8 +58,8 @@ def build(verbose: bool = False) -> Path:
             print(out)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}): {' '.join(cmd)}")
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

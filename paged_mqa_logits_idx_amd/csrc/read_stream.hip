@@ -1,0 +1,122 @@
+// Bare key-page read stream: the reachable HBM read rate for the decode's
+// access pattern on this chip, used by the benchmark as the measured
+// denominator next to the 8 TB/s peak.
+//
+// Each wave of a fixed grid (two 256-thread workgroups per CU, as the decode
+// launches) takes every (total waves)-th entry of a list of page ids and
+// copies that 8,448-byte page (8 KiB of e4m3 codes, 256 B of scales) into one
+// of two LDS slots of its own, with the same instructions, chunk order and
+// non-temporal cache policy as the decode: eight 16-byte-per-lane
+// global_load_lds and one 4-byte-per-lane for the scales.  Before a slot is
+// refilled the wave waits for that slot's previous page (the decode's two-page
+// ring).  Nothing is computed and nothing is stored but one word per wave at
+// the end.  With `registers` set, the same pages go into VGPRs with ordinary
+// 16-byte loads instead (the register-stream comparison).
+//
+// Not part of the indexer: the library exports only this calibration call.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace {
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef __attribute__((address_space(1))) const void* global_ptr;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kPageBytes = 8448;
+constexpr int kWaves = 4;
+constexpr int kNt = 2;  // nt bit of the cache-policy operand
+constexpr int kOpsPerPage = 9;
+
+// s_waitcnt immediate waiting on vmcnt only (vmcnt[3:0], expcnt[6:4],
+// lgkmcnt[11:8], vmcnt[5:4] at bits 15:14).
+constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
+
+// ids[p] for a wave-uniform p, read through the scalar cache (a vector load
+// would enter the vmcnt order that the ring's waits count).
+__device__ __forceinline__ int32_t page_id(const int32_t* ids, int32_t p) {
+  typedef __attribute__((address_space(4))) const int32_t* const_i32;
+  return ((const_i32)(uintptr_t)ids)[__builtin_amdgcn_readfirstlane(p)];
+}
+
+__device__ __forceinline__ void dma_page(const uint8_t* page, lds_u8* slot, int lane) {
+  const int rsub = lane >> 3, c = lane & 7;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int i = 8 * t + rsub;
+    __builtin_amdgcn_global_load_lds((global_ptr)(page + i * 128 + 16 * (c ^ (i & 7))),
+                                     (lds_ptr)(slot + 1024 * t), 16, 0, kNt);
+  }
+  __builtin_amdgcn_global_load_lds((global_ptr)(page + 8192 + 4 * lane), (lds_ptr)(slot + 8192), 4, 0, kNt);
+}
+
+__global__ __launch_bounds__(256) void dma_stream_kernel(const uint8_t* pool, const int32_t* ids, int32_t n,
+                                                         uint32_t* sink) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves * 2 * kPageBytes];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int gw = blockIdx.x * kWaves + wave, nw = gridDim.x * kWaves;
+  lds_u8* slots = (lds_u8*)(lds + wave * 2 * kPageBytes);
+  int t = 0;
+  for (int32_t p = gw; p < n; p += nw, ++t) {
+    if (t >= 2) __builtin_amdgcn_s_waitcnt(wait_vm(kOpsPerPage));  // the page two back has landed
+    const int32_t id = page_id(ids, p);
+    dma_page(pool + (int64_t)id * kPageBytes, slots + (t & 1) * kPageBytes, lane);
+  }
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));
+  __syncthreads();
+  if (lane == 0) sink[gw] = lds[wave * 2 * kPageBytes + 8192];
+}
+
+__global__ __launch_bounds__(256) void reg_stream_kernel(const uint8_t* pool, const int32_t* ids, int32_t n,
+                                                         uint32_t* sink) {
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int gw = blockIdx.x * kWaves + wave, nw = gridDim.x * kWaves;
+  uint32_t acc = 0u;
+  for (int32_t p = gw; p < n; p += nw) {
+    const int32_t id = page_id(ids, p);
+    const uint8_t* page = pool + (int64_t)id * kPageBytes;
+    u32x4 v[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      v[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(page + 1024 * t + 16 * lane));
+    const uint32_t s = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(page + 8192 + 4 * lane));
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc ^= v[t][0] ^ v[t][1] ^ v[t][2] ^ v[t][3];
+    acc ^= s;
+  }
+  if (acc == 0x9E3779B9u) sink[gw] = acc;  // keeps the loads; almost never stores
+}
+
+}  // namespace
+
+// Reads the n pages pool[ids[i] * 8448 ...] once each on `stream` (asynchronous).
+// pool: device, >= (max id + 1) * 8448 bytes, 16-byte aligned; ids: device
+// int32[n], each in range (not checked on the device); sink: device
+// uint32[2 * CUs * 4], written with arbitrary words.  registers: 0 = LDS DMA
+// (the decode's path), 1 = 16-byte loads into VGPRs.  Returns 0, or -1 for a
+// null pointer / negative n / misaligned pool, or the HIP error of the launch.
+extern "C" int idx_read_stream(const void* pool, const int32_t* ids, int32_t n, uint32_t* sink,
+                               int32_t registers, hipStream_t stream) {
+  if (!pool || !ids || !sink || n < 0 || (reinterpret_cast<uintptr_t>(pool) & 15u) != 0u) return -1;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                               hipSuccess || cus <= 0)
+    return -1;
+  const dim3 grid(2 * cus), block(256);
+  if (registers)
+    reg_stream_kernel<<<grid, block, 0, stream>>>(static_cast<const uint8_t*>(pool), ids, n, sink);
+  else
+    dma_stream_kernel<<<grid, block, 0, stream>>>(static_cast<const uint8_t*>(pool), ids, n, sink);
+  return (int)hipGetLastError();
+}
+
+// Workgroups the launch above uses (the sink holds 4 words per workgroup).
+extern "C" int idx_read_stream_workgroups(void) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                               hipSuccess)
+    return -1;
+  return 2 * cus;
+}
