@@ -251,7 +251,7 @@ def achievable_peaks():
     return round(copy_gbs, 1), round(mm_tflops, 1)
 
 
-def read_stream_rates(same_pages: int):
+def read_stream_rates(same_pages: int, settle: bool = True):
     """Reachable HBM read rate of the decode's access pattern, measured here:
     the bare key-page read stream of libidx_read_stream.so (random 8448-byte
     pages into LDS by DMA, nt policy, the decode's grid; nothing computed or
@@ -282,7 +282,7 @@ def read_stream_rates(same_pages: int):
                                      sink.data_ptr(), 0, torch.cuda.current_stream().cuda_stream)
             if rc != 0:
                 raise RuntimeError(f"idx_read_stream failed ({rc})")
-        return time_graph(step, 20, 5, settle=True)[0] / 20
+        return time_graph(step, 20, 5, settle=settle)[0] / 20
 
     t_all = timed(STREAM_POOL_PAGES)
     n = max(1, min(int(same_pages), STREAM_POOL_PAGES // 2))
@@ -397,6 +397,60 @@ def traffic_for(cfg_key: str, launches_alg_bytes: float):
     return ent.get("bytes_per_launch")
 
 
+def logits_line(c, steps: int, warm: int, stream_gbs=None, mm_tflops=None, settle: bool = True) -> dict:
+    """One secondary logits line: the call timed after a settled warm-up."""
+    _, r = measure(c, steps, warm, settle=settle)
+    log(json.dumps(r))
+    entry = {
+        "workload": r["name"], "kernel_ms_mean": round(r["kernel_ms_mean"], 5),
+        "positions_per_s": r["positions_per_s_kernel"], "steps": steps,
+        "untimed_replays": r["untimed_replays"],
+    }
+    if r["shared_table"] or c == "varlen":  # prefill: one key read serves many rows
+        entry.update(bound="mfma", achieved_tflops=round(r["tflops"], 2), peak_tflops=BF16_MFMA_PEAK_TFLOPS,
+                     frac=round(r["tflops"] / BF16_MFMA_PEAK_TFLOPS, 4), alg_flops=r["alg_flops"])
+        if mm_tflops:
+            entry["frac_of_matmul"] = round(r["tflops"] / mm_tflops, 4)
+    else:
+        entry.update(bound="hbm", achieved_gbs=round(r["gbs"], 1), peak_gbs=HBM_PEAK_GBS,
+                     frac=round(r["gbs"] / HBM_PEAK_GBS, 4),
+                     alg_bytes=r["alg_read_bytes"] + r["alg_write_bytes"])
+        if stream_gbs:
+            entry["frac_of_stream"] = round(r["gbs"] / stream_gbs, 4)
+    entry["traffic"] = traffic_for(str(c), 0)
+    return entry
+
+
+def topk_line(c, steps: int, warm: int, settle: bool = True) -> dict:
+    """The fused logits + top-k call on configuration c, and the top-k kernel
+    alone over the logits it left (HBM roofline: 4 B per live logit read, 4 B
+    per selected index written)."""
+    wl, r = measure(c, steps, warm, topk=TOPK, settle=settle)
+    log(json.dumps(r))
+    tk_bytes = 4 * wl.live_positions() + 4 * TOPK * wl.rows
+    tk_gbs = tk_bytes / (r["topk_only_ms"] * 1e-3) / 1e9
+    return {
+        "workload": f"{r['name']}, logits + top-{TOPK} (fused call, no -inf tail)",
+        "k": TOPK, "kernel_ms_mean": round(r["kernel_ms_mean"], 5),
+        "topk_only_ms": round(r["topk_only_ms"], 5),
+        "positions_per_s": r["positions_per_s_kernel"], "steps": steps,
+        "untimed_replays": r["untimed_replays"],
+        "topk_roofline": {"bound": "hbm", "achieved": round(tk_gbs, 1), "peak": HBM_PEAK_GBS,
+                          "unit": "GB/s", "frac": round(tk_gbs / HBM_PEAK_GBS, 4),
+                          "alg_bytes": tk_bytes, "traffic": traffic_for(f"topk_{c}", 0)},
+    }
+
+
+def store_line(steps: int, warm: int, stream_gbs=None, settle: bool = True) -> dict:
+    r = measure_store(steps, warm, settle=settle)
+    if stream_gbs:
+        r["frac_of_stream"] = round(r["achieved_gbs"] / stream_gbs, 4)
+    r["steps"] = steps
+    r["traffic"] = traffic_for("store_fp8", 0)
+    log(json.dumps(r))
+    return r
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -412,6 +466,11 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a device copy of 1 GiB (counter calibration)")
+    ap.add_argument("--no-settle", action="store_true",
+                    help="with --only: no settling replays (counter-collection runs)")
+    ap.add_argument("--only", default=None,
+                    help="run one secondary line alone and print it (for profiling): 2, 3c, 4, 2b, "
+                         "4f, varlen, 3, topk_3, topk_4, store_fp8 or read_stream")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -433,6 +492,21 @@ def main() -> int:
         log("copied 1 GiB x5")
         return 0
 
+    if args.only is not None:
+        steps, warm, settle = args.steps, args.warmup, not args.no_settle
+        o = args.only
+        if o.startswith("topk_"):
+            c = o[5:]
+            entry = topk_line(int(c) if c.isdigit() else c, steps, warm, settle)
+        elif o == "store_fp8":
+            entry = store_line(steps, warm, settle=settle)
+        elif o == "read_stream":
+            entry = read_stream_rates(15389, settle)
+        else:
+            entry = logits_line(int(o) if o.isdigit() else o, steps, warm, settle=settle)
+        print(json.dumps({"only": o, **entry}), flush=True)
+        return 0
+
     cfg = int(args.workload) if args.workload.isdigit() else args.workload
     wl, main_res = measure(cfg, args.steps, args.warmup)
     log(json.dumps(main_res))
@@ -448,50 +522,11 @@ def main() -> int:
     secondary = {}
     if not args.no_secondary:
         for c in (2, "3c", 4, "2b", "4f", "varlen"):
-            if str(c) == str(cfg):
-                continue
-            _, r = measure(c, sec_steps, sec_warm, settle=True)
-            log(json.dumps(r))
-            entry = {
-                "workload": r["name"], "kernel_ms_mean": round(r["kernel_ms_mean"], 5),
-                "positions_per_s": r["positions_per_s_kernel"], "steps": sec_steps,
-                "untimed_replays": r["untimed_replays"],
-            }
-            if r["shared_table"] or c == "varlen":  # prefill: one key read serves many rows
-                entry.update(bound="mfma", achieved_tflops=round(r["tflops"], 2),
-                             peak_tflops=BF16_MFMA_PEAK_TFLOPS,
-                             frac=round(r["tflops"] / BF16_MFMA_PEAK_TFLOPS, 4),
-                             frac_of_matmul=round(r["tflops"] / mm_tflops, 4),
-                             alg_flops=r["alg_flops"])
-            else:
-                entry.update(bound="hbm", achieved_gbs=round(r["gbs"], 1), peak_gbs=HBM_PEAK_GBS,
-                             frac=round(r["gbs"] / HBM_PEAK_GBS, 4),
-                             frac_of_stream=round(r["gbs"] / stream_gbs, 4),
-                             alg_bytes=r["alg_read_bytes"] + r["alg_write_bytes"])
-            entry["traffic"] = traffic_for(str(c), 0)
-            secondary[str(c)] = entry
+            if str(c) != str(cfg):
+                secondary[str(c)] = logits_line(c, sec_steps, sec_warm, stream_gbs, mm_tflops)
         for c in (cfg, 4):
-            twl, r = measure(c, sec_steps, sec_warm, topk=TOPK, settle=True)
-            log(json.dumps(r))
-            # top-k kernel alone: reads each row's live logits, writes k indices per row
-            tk_bytes = 4 * twl.live_positions() + 4 * TOPK * twl.rows
-            tk_gbs = tk_bytes / (r["topk_only_ms"] * 1e-3) / 1e9
-            secondary[f"topk_{c}"] = {
-                "workload": f"{r['name']}, logits + top-{TOPK} (fused call, no -inf tail)",
-                "k": TOPK, "kernel_ms_mean": round(r["kernel_ms_mean"], 5),
-                "topk_only_ms": round(r["topk_only_ms"], 5),
-                "positions_per_s": r["positions_per_s_kernel"], "steps": sec_steps,
-                "untimed_replays": r["untimed_replays"],
-                "topk_roofline": {"bound": "hbm", "achieved": round(tk_gbs, 1), "peak": HBM_PEAK_GBS,
-                                  "unit": "GB/s", "frac": round(tk_gbs / HBM_PEAK_GBS, 4),
-                                  "alg_bytes": tk_bytes, "traffic": traffic_for(f"topk_{c}", 0)},
-            }
-        r = measure_store(sec_steps, sec_warm, settle=True)
-        r["frac_of_stream"] = round(r["achieved_gbs"] / stream_gbs, 4)
-        r["steps"] = sec_steps
-        r["traffic"] = traffic_for("store_fp8", 0)
-        log(json.dumps(r))
-        secondary["store_fp8"] = r
+            secondary[f"topk_{c}"] = topk_line(c, sec_steps, sec_warm)
+        secondary["store_fp8"] = store_line(sec_steps, sec_warm, stream_gbs)
 
     cpu = None
     if not args.no_cpu_baseline:
