@@ -87,6 +87,7 @@ struct Params {
   const float* w;     // [rows][64]
   float* out;         // [rows][width*64]
   int64_t num_pages, kv_stride, ks_stride, pt_stride;
+  uint32_t pages_lim;  // min(num_pages, 2^31): page ids below it are in the pool (a 32-bit scalar compare)
   int32_t rows, width;
   int32_t fill;       // 0: page slots past a row's live pages are left unwritten
   const int32_t* rt;  // shared kernel: table index of each row (NULL: table 0 for all)
@@ -285,8 +286,8 @@ __device__ __forceinline__ int32_t clamp_len(int32_t L, int32_t width) {
   return min(max(L, 0), width * kPage);
 }
 
-__device__ __forceinline__ bool page_ok(int32_t gp, int64_t num_pages) {
-  return gp >= 0 && (int64_t)gp < num_pages;
+__device__ __forceinline__ bool page_ok(int32_t gp, uint32_t pages_lim) {
+  return gp >= 0 && (uint32_t)gp < pages_lim;
 }
 
 // Wave-uniform values kept in scalar registers.
@@ -372,7 +373,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(KEY 
       const int32_t* tab = p.pt + (int64_t)b * p.pt_stride;
       PageKeys<KEY> buf[2];
       int32_t gcur = load_uniform(tab, j0);
-      bool okcur = page_ok(gcur, p.num_pages);
+      bool okcur = page_ok(gcur, p.pages_lim);
       if (okcur) load_page_global<KEY>(p, gcur, lane, buf[0]);
 #pragma unroll
       for (int t = 0; t < PPW; ++t) {
@@ -382,7 +383,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(KEY 
           bool oknxt = false;
           if (t + 1 < PPW && j + 1 < jl) {
             gnxt = load_uniform(tab, j + 1);
-            oknxt = page_ok(gnxt, p.num_pages);
+            oknxt = page_ok(gnxt, p.pages_lim);
             if (oknxt) load_page_global<KEY>(p, gnxt, lane, buf[(t + 1) & 1]);
           }
           if (okcur)
@@ -657,7 +658,7 @@ __device__ __forceinline__ void row_pages_dma_bf16(const Params& p, int32_t b, i
   const uint8_t* safe = p.q + (int64_t)b * (kHeads * kDim * 2);
   const int32_t J = jb - ja;
   const int32_t g0 = load_uniform(tab, ja);
-  bool ok = page_ok(g0, p.num_pages);
+  bool ok = page_ok(g0, p.pages_lim);
   dma_page_bf16(ok ? p.kv + (int64_t)g0 * p.kv_stride : safe, slot, lane);
   // The query was requested before the DMA: wait for it here with the DMA in
   // flight, so that no conservative wait lands in the page loop.
@@ -673,7 +674,7 @@ __device__ __forceinline__ void row_pages_dma_bf16(const Params& p, int32_t b, i
     const int32_t g = g_ahead;
     g_ahead = (tt + 2 < J) ? load_uniform(tab, ja + tt + 2) : -1;
     if (tt + 1 < J) {
-      ok = page_ok(g, p.num_pages);
+      ok = page_ok(g, p.pages_lim);
       dma_page_bf16(ok ? p.kv + (int64_t)g * p.kv_stride : safe, slot, lane);
     }
     score_buffer_put(out, cur_ok, cur_ok ? score_page<kBf16>(rq, pk, lane) : 0.f, L, lane);
@@ -700,7 +701,7 @@ __device__ __forceinline__ void row_pages_dma(const Params& p, int32_t b, int32_
     // (a short segment still issues NS groups, the extra ones from the query
     // row, so that the prologue always holds NS groups)
     const int32_t g = t < J ? load_uniform(tab, ja + t) : -1;
-    ok[t] = page_ok(g, p.num_pages);
+    ok[t] = page_ok(g, p.pages_lim);
     const uint8_t* keys = ok[t] ? p.kv + (int64_t)g * p.kv_stride : safe;
     const uint8_t* sc = ok[t] ? p.ks + (int64_t)g * p.ks_stride : safe + 8192;
     dma_page(keys, sc, slots + t * kSlotBytes, lane);
@@ -736,7 +737,7 @@ __device__ __forceinline__ void row_pages_dma(const Params& p, int32_t b, int32_
         const int32_t g = g_ahead;
         g_ahead = (tt + NS + 1 < J) ? load_uniform(tab, ja + tt + NS + 1) : -1;
         if (tt + NS < J) {
-          ok[u] = page_ok(g, p.num_pages);
+          ok[u] = page_ok(g, p.pages_lim);
           const uint8_t* keys = ok[u] ? p.kv + (int64_t)g * p.kv_stride : safe;
           const uint8_t* sc = ok[u] ? p.ks + (int64_t)g * p.ks_stride : safe + 8192;
           dma_page(keys, sc, slot, lane);
@@ -871,22 +872,25 @@ constexpr int32_t shared_dma_ops(int wave) {
 template <int KEY>
 __device__ __forceinline__ void shared_dma_page(const uint8_t* page, const uint8_t* scales, lds_u8* slot,
                                                 int wave, int lane) {
+  // The lane's source offsets are 32-bit and the page address wave-uniform,
+  // so each DMA takes the scalar base + vector offset form (no 64-bit
+  // address arithmetic per page).
   const int r0 = kSharedRowsPerWave * wave;
   if constexpr (KEY == kBf16) {
     // rows of 256 B, 4 per DMA
 #pragma unroll
     for (int t = 0; t < kSharedRowsPerWave / 4; ++t) {
       const int i = r0 + 4 * t + (lane >> 4), c = lane & 15;
-      __builtin_amdgcn_global_load_lds((global_ptr)(page + i * 256 + 16 * (c ^ (i & 15))),
-                                       (lds_ptr)(slot + (r0 + 4 * t) * 256), 16, 0, 0);
+      const uint32_t off = (uint32_t)(i * 256 + 16 * (c ^ (i & 15)));
+      __builtin_amdgcn_global_load_lds((global_ptr)(page + off), (lds_ptr)(slot + (r0 + 4 * t) * 256), 16, 0, 0);
     }
   } else {
     // rows of 128 B, 8 per DMA
 #pragma unroll
     for (int t = 0; t < kSharedRowsPerWave / 8; ++t) {
       const int i = r0 + 8 * t + (lane >> 3), c = lane & 7;
-      __builtin_amdgcn_global_load_lds((global_ptr)(page + i * 128 + 16 * (c ^ (i & 7))),
-                                       (lds_ptr)(slot + (r0 + 8 * t) * 128), 16, 0, 0);
+      const uint32_t off = (uint32_t)(i * 128 + 16 * (c ^ (i & 7)));
+      __builtin_amdgcn_global_load_lds((global_ptr)(page + off), (lds_ptr)(slot + (r0 + 8 * t) * 128), 16, 0, 0);
     }
     if (wave == 0)
       __builtin_amdgcn_global_load_lds((global_ptr)(scales + 4 * lane), (lds_ptr)(slot + 8192), 4, 0, 0);
@@ -920,25 +924,48 @@ __device__ __forceinline__ void wait_vm_n(int32_t n) {
 // overlap the next page's DMA issue.
 typedef __attribute__((address_space(3))) const u32x4 lds_u32x4c;
 typedef __attribute__((address_space(3))) const float lds_f32c;
+// The lane's byte offsets in a slot of its fragments of position block 0 (a
+// block adds 4096 bytes for bf16, 2048 for fp8) and of its scale: computed once,
+// so that a page costs one add per offset and the block steps are immediate
+// offsets of the LDS loads.
+struct SharedSlotOffsets {
+  uint32_t o[4];
+};
 template <int KEY>
-__device__ __forceinline__ void read_shared_slot(uint32_t sb, int lane, PageKeys<KEY>& pk) {
+__device__ __forceinline__ SharedSlotOffsets shared_slot_offsets(int lane) {
+  SharedSlotOffsets so;
+  const int n = lane & 15, g = lane >> 4;
   if constexpr (KEY == kBf16) {
-    const int n = lane & 15, g = lane >> 4;
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int v = 0; v < 4; ++v) so.o[v] = (uint32_t)(n * 256 + 16 * ((8 * (v >> 1) + 2 * g + (v & 1)) ^ n));
+  } else {
+    so.o[0] = slot_chunk_offset(lane, 0);
+    so.o[1] = slot_chunk_offset(lane, 1);
+    so.o[2] = (uint32_t)(8192 + 4 * lane);
+    so.o[3] = 0u;
+  }
+  return so;
+}
+
+template <int KEY>
+__device__ __forceinline__ void read_shared_slot(uint32_t sb, const SharedSlotOffsets& so, PageKeys<KEY>& pk) {
+  if constexpr (KEY == kBf16) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
-        pk.v[nb][v] = *(lds_u32x4c*)(size_t)(sb + (uint32_t)(n * 256 + 16 * ((8 * (v >> 1) + 2 * g + (v & 1)) ^ n)) +
-                                             4096 * nb);
+    for (int v = 0; v < 4; ++v) {
+      lds_u32x4c* src = (lds_u32x4c*)(size_t)(sb + so.o[v]);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) pk.v[nb][v] = src[256 * nb];
+    }
     pk.s = 1.0f;
   } else {
-    const uint32_t a0 = sb + slot_chunk_offset(lane, 0), a1 = sb + slot_chunk_offset(lane, 1);
+    lds_u32x4c* s0 = (lds_u32x4c*)(size_t)(sb + so.o[0]);
+    lds_u32x4c* s1 = (lds_u32x4c*)(size_t)(sb + so.o[1]);
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
-      pk.v[nb][0] = *(lds_u32x4c*)(size_t)(a0 + 2048 * nb);
-      pk.v[nb][1] = *(lds_u32x4c*)(size_t)(a1 + 2048 * nb);
+      pk.v[nb][0] = s0[128 * nb];
+      pk.v[nb][1] = s1[128 * nb];
     }
-    pk.s = *(lds_f32c*)(size_t)(sb + 8192 + 4 * lane);
+    pk.s = *(lds_f32c*)(size_t)(sb + so.o[2]);
   }
 }
 
@@ -966,6 +993,7 @@ __global__ __launch_bounds__(64 * kSharedRows) __attribute__((amdgpu_waves_per_e
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int32_t ops = shared_dma_ops<KEY>(wave);  // DMA operations per page
+  const SharedSlotOffsets so = shared_slot_offsets<KEY>(lane);
   lds_f32* sbuf = (lds_f32*)(lds_raw + NS * kSlot + wave * kSharedScoreBufPages * kPage * 4);
   const int32_t width = p.width;
 
@@ -1042,7 +1070,11 @@ __global__ __launch_bounds__(64 * kSharedRows) __attribute__((amdgpu_waves_per_e
         // A page id outside the pool -- or a page past jl, issued only to keep
         // the operation count per iteration constant -- is copied from the
         // query buffer instead (always valid memory, at least 16 KiB).
-        uint32_t ok_bits = 0;  // bit t % NS: page j0 + t has a valid id
+        // Page id whose DMA each slot holds (scalar selects on the slot index,
+        // no per-page vector work).
+        int32_t slot_id[NS];
+#pragma unroll
+        for (int v = 0; v < NS; ++v) slot_id[v] = -1;
         // Table entry of page j0 + t (-1 past the pages any row needs).  Read
         // one iteration before its DMA is issued, so that the scalar load's
         // latency is not on the page loop's path.
@@ -1051,9 +1083,11 @@ __global__ __launch_bounds__(64 * kSharedRows) __attribute__((amdgpu_waves_per_e
           return (j < jl && table_ok) ? load_uniform(tab, j) : -1;
         };
         auto issue = [&](int32_t t, int32_t g) {
-          const bool ok = page_ok(g, p.num_pages);
+          const bool ok = page_ok(g, p.pages_lim);
           const int u = t % NS;
-          ok_bits = (uint32_t)uniform((int32_t)((ok_bits & ~(1u << u)) | ((ok ? 1u : 0u) << u)));
+#pragma unroll
+          for (int v = 0; v < NS; ++v)
+            if (v == u) slot_id[v] = g;
           const uint8_t* page = ok ? p.kv + (int64_t)g * p.kv_stride : p.q;
           const uint8_t* sc = (KEY == kFp8 && ok) ? p.ks + (int64_t)g * p.ks_stride : p.q + 8192;
           shared_dma_page<KEY>(page, sc, slots + u * kSlot, wave, lane);
@@ -1085,11 +1119,15 @@ __global__ __launch_bounds__(64 * kSharedRows) __attribute__((amdgpu_waves_per_e
           __builtin_amdgcn_s_barrier();
           __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
           PageKeys<KEY> pk;
-          if (row_ok && j < live_w) read_shared_slot<KEY>(base + (uint32_t)(u * kSlot), lane, pk);
+          if (row_ok && j < live_w) read_shared_slot<KEY>(base + (uint32_t)(u * kSlot), so, pk);
           issue(t + NS - 1, g_next);
           g_next = table_entry(t + NS);
           if (row_ok) {  // (a page past this row's length is all -inf)
-            const bool valid = (ok_bits >> u) & 1u;
+            int32_t gu = slot_id[0];
+#pragma unroll
+            for (int v = 1; v < NS; ++v)
+              if (v == u) gu = slot_id[v];
+            const bool valid = page_ok(gu, p.pages_lim);
             score_buffer_put(logits, valid, (j < live_w && valid) ? score_page<KEY>(rq, pk, lane) : 0.f,
                              L, lane);
           }
@@ -1709,6 +1747,7 @@ int launch(const void* q, const void* kv_pages, const float* kscale, const int32
   p.w = weights;
   p.out = out;
   p.num_pages = num_pages;
+  p.pages_lim = (uint32_t)(num_pages < ((int64_t)1 << 31) ? num_pages : ((int64_t)1 << 31));
   p.kv_stride = kv_page_stride;
   p.ks_stride = (KEY == kFp8) ? kscale_page_stride : 0;
   p.pt_stride = page_table_row_stride;
