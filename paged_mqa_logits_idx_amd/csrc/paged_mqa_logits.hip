@@ -496,45 +496,17 @@ __device__ __forceinline__ void read_slot(uint32_t a0, uint32_t a1, uint32_t a4,
       : "memory");
 }
 
-// Wait until at most n_after vector-memory operations are outstanding (n_after
-// <= 31: up to 4 slots), then read the slot.
-__device__ __forceinline__ void read_slot_after(int n_after, uint32_t a0, uint32_t a1, uint32_t a4,
+// Wait until at most `groups` page DMA groups (kDmaOps operations each) are
+// outstanding, then read the slot.  groups < NS, so the wait is one of NS
+// immediates: one scalar compare per page (a switch over every possible count
+// compiled to a branch tree).
+template <int NS>
+__device__ __forceinline__ void read_slot_after(int groups, uint32_t a0, uint32_t a1, uint32_t a4,
                                                 PageKeys<kFp8>& pk) {
-  switch (n_after) {
-    case 0: read_slot<0>(a0, a1, a4, pk); break;
-    case 1: read_slot<1>(a0, a1, a4, pk); break;
-    case 2: read_slot<2>(a0, a1, a4, pk); break;
-    case 3: read_slot<3>(a0, a1, a4, pk); break;
-    case 4: read_slot<4>(a0, a1, a4, pk); break;
-    case 5: read_slot<5>(a0, a1, a4, pk); break;
-    case 6: read_slot<6>(a0, a1, a4, pk); break;
-    case 7: read_slot<7>(a0, a1, a4, pk); break;
-    case 8: read_slot<8>(a0, a1, a4, pk); break;
-    case 9: read_slot<9>(a0, a1, a4, pk); break;
-    case 10: read_slot<10>(a0, a1, a4, pk); break;
-    case 11: read_slot<11>(a0, a1, a4, pk); break;
-    case 12: read_slot<12>(a0, a1, a4, pk); break;
-    case 13: read_slot<13>(a0, a1, a4, pk); break;
-    case 14: read_slot<14>(a0, a1, a4, pk); break;
-    case 15: read_slot<15>(a0, a1, a4, pk); break;
-    case 16: read_slot<16>(a0, a1, a4, pk); break;
-    case 17: read_slot<17>(a0, a1, a4, pk); break;
-    case 18: read_slot<18>(a0, a1, a4, pk); break;
-    case 19: read_slot<19>(a0, a1, a4, pk); break;
-    case 20: read_slot<20>(a0, a1, a4, pk); break;
-    case 21: read_slot<21>(a0, a1, a4, pk); break;
-    case 22: read_slot<22>(a0, a1, a4, pk); break;
-    case 23: read_slot<23>(a0, a1, a4, pk); break;
-    case 24: read_slot<24>(a0, a1, a4, pk); break;
-    case 25: read_slot<25>(a0, a1, a4, pk); break;
-    case 26: read_slot<26>(a0, a1, a4, pk); break;
-    case 27: read_slot<27>(a0, a1, a4, pk); break;
-    case 28: read_slot<28>(a0, a1, a4, pk); break;
-    case 29: read_slot<29>(a0, a1, a4, pk); break;
-    case 30: read_slot<30>(a0, a1, a4, pk); break;
-    case 31: read_slot<31>(a0, a1, a4, pk); break;
-    default: read_slot<0>(a0, a1, a4, pk); break;
-  }
+  static_assert(NS >= 1 && NS <= 3, "one to three DMA slots");
+  if (NS > 2 && groups == 2) read_slot<2 * kDmaOps>(a0, a1, a4, pk);
+  else if (NS > 1 && groups == 1) read_slot<kDmaOps>(a0, a1, a4, pk);
+  else read_slot<0>(a0, a1, a4, pk);
 }
 
 // Boundary of wave wid's share of `total` units when the first h waves weigh
@@ -730,9 +702,8 @@ __device__ __forceinline__ void row_pages_dma(const Params& p, int32_t b, int32_
         // buffer flush are not counted: the wait then also covers them.)
         const int32_t lo = max(0, tt - NS + 1), hi = min(tt - 1, J - NS - 1);
         const int32_t groups = (tt < NS ? NS - 1 - tt : 0) + max(0, hi - lo + 1);
-        const int32_t n_after = kDmaOps * groups;
         PageKeys<kFp8> pk;
-        read_slot_after(uniform(n_after), a0, a1, a4, pk);
+        read_slot_after<NS>(uniform(groups), a0, a1, a4, pk);
         const bool cur_ok = ok[u];
         const int32_t g = g_ahead;
         g_ahead = (tt + NS + 1 < J) ? load_uniform(tab, ja + tt + NS + 1) : -1;
