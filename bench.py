@@ -251,14 +251,17 @@ def achievable_peaks():
     return round(copy_gbs, 1), round(mm_tflops, 1)
 
 
-def read_stream_rates(same_pages: int, settle: bool = True):
+def read_stream_rates(same_pages: int, settle: bool = True, out_bytes: int = 0):
     """Reachable HBM read rate of the decode's access pattern, measured here:
     the bare key-page read stream of libidx_read_stream.so (random 8448-byte
     pages into LDS by DMA, nt policy, the decode's grid; nothing computed or
     stored).  Returns the rate over the whole 1.1 GB pool per launch, the
     marginal rate between that and `same_pages` pages, and the time for
     `same_pages` pages (launches rotate over disjoint page sets, >= 1 GB
-    apart, so no launch finds its pages in the last-level cache)."""
+    apart, so no launch finds its pages in the last-level cache).  With
+    out_bytes, also the time of the same page reads plus out_bytes of -inf
+    writes in the decode's order (the first half of the grid writes first):
+    the bare traffic of one decode launch, output buffers rotated too."""
     import ctypes
 
     import torch
@@ -268,6 +271,9 @@ def read_stream_rates(same_pages: int, settle: bool = True):
                                     ctypes.c_int32, ctypes.c_void_p]
     lib.idx_read_stream.restype = ctypes.c_int
     lib.idx_read_stream_workgroups.restype = ctypes.c_int
+    lib.idx_read_write_stream.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                          ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    lib.idx_read_write_stream.restype = ctypes.c_int
     page = 8448
     pool = torch.ones(STREAM_POOL_PAGES * page, dtype=torch.uint8, device="cuda")
     gen = torch.Generator().manual_seed(7)
@@ -288,11 +294,32 @@ def read_stream_rates(same_pages: int, settle: bool = True):
     n = max(1, min(int(same_pages), STREAM_POOL_PAGES // 2))
     t_same = timed(n)
     b_all, b_same = STREAM_POOL_PAGES * page, n * page
+    res = {"dma_read_stream_gbs": round(b_all / (t_all * 1e-3) / 1e9, 1),
+           "dma_read_stream_marginal_gbs": round((b_all - b_same) / ((t_all - t_same) * 1e-3) / 1e9, 1),
+           "dma_read_same_pages": n, "dma_read_same_pages_us": round(t_same * 1e3, 2)}
+    if out_bytes:
+        sets = max(1, STREAM_POOL_PAGES // n)
+        outs = [torch.empty(out_bytes // 4, dtype=torch.float32, device="cuda")
+                for _ in range(max(2, min(16, math.ceil(ROTATE_BYTES / out_bytes))))]
+
+        def rw_time(order):
+            def rw_step(i):
+                rc = lib.idx_read_write_stream(pool.data_ptr(), ids.data_ptr() + 4 * n * (i % sets), n,
+                                               outs[i % len(outs)].data_ptr(), out_bytes, order, sink.data_ptr(),
+                                               torch.cuda.current_stream().cuda_stream)
+                if rc != 0:
+                    raise RuntimeError(f"idx_read_write_stream failed ({rc})")
+            return time_graph(rw_step, 20, 5, settle=settle)[0] / 20 * 1e3
+        # orders: half the grid writes first (the decode's), all write first,
+        # all read first, writes spread over the reads; the fastest is the bound
+        t_rw = {name: round(rw_time(o), 2) for o, name in enumerate(("half_first", "writes_first",
+                                                                      "reads_first", "interleaved"))}
+        res.update(bare_read_write_us=min(t_rw.values()), bare_read_write_by_order_us=t_rw,
+                   bare_write_bytes=out_bytes)
+        del outs
     del pool, ids, sink
     torch.cuda.empty_cache()
-    return {"dma_read_stream_gbs": round(b_all / (t_all * 1e-3) / 1e9, 1),
-            "dma_read_stream_marginal_gbs": round((b_all - b_same) / ((t_all - t_same) * 1e-3) / 1e9, 1),
-            "dma_read_same_pages": n, "dma_read_same_pages_us": round(t_same * 1e3, 2)}
+    return res
 
 
 def measure_store(steps: int, warmup: int, settle: bool = False):
@@ -501,7 +528,7 @@ def main() -> int:
         elif o == "store_fp8":
             entry = store_line(steps, warm, settle=settle)
         elif o == "read_stream":
-            entry = read_stream_rates(15389, settle)
+            entry = read_stream_rates(15389, settle, out_bytes=64 * 4097 * 64 * 4)
         else:
             entry = logits_line(int(o) if o.isdigit() else o, steps, warm, settle=settle)
         print(json.dumps({"only": o, **entry}), flush=True)
@@ -511,7 +538,7 @@ def main() -> int:
     wl, main_res = measure(cfg, args.steps, args.warmup)
     log(json.dumps(main_res))
     copy_gbs, mm_tflops = achievable_peaks()
-    stream = read_stream_rates(main_res["live_pages"])
+    stream = read_stream_rates(main_res["live_pages"], out_bytes=main_res["alg_write_bytes"])
     stream_gbs = stream["dma_read_stream_gbs"]
     log(f"achievable: key-page read stream {json.dumps(stream)}, torch device copy {copy_gbs} GB/s, "
         f"bf16 8192^3 matmul {mm_tflops} TFLOP/s")
@@ -554,6 +581,8 @@ def main() -> int:
                     "alg_bytes_per_launch": alg_bytes,
                     "kernel_ms_mean": round(main_res["kernel_ms_mean"], 5),
                     "achievable": {**stream, "frac_of_stream": round(achieved / stream_gbs, 4),
+                                   **({"kernel_vs_bare_traffic": round(stream["bare_read_write_us"] / (
+                                       main_res["kernel_ms_mean"] * 1e3), 4)} if "bare_read_write_us" in stream else {}),
                                    "torch_device_copy_gbs": copy_gbs,
                                    "bf16_matmul_tflops": mm_tflops}}
     out = {

@@ -13,6 +13,11 @@
 // the end.  With `registers` set, the same pages go into VGPRs with ordinary
 // 16-byte loads instead (the register-stream comparison).
 //
+// The read-write variant adds the decode's other traffic: each wave also
+// writes an equal contiguous share of an output buffer with 16-byte
+// non-temporal stores of -inf -- workgroups of the grid's first half before
+// their pages, the second half after them, as the decode orders its fill.
+//
 // Not part of the indexer: the library exports only this calibration call.
 #include <hip/hip_runtime.h>
 
@@ -52,18 +57,38 @@ __device__ __forceinline__ void dma_page(const uint8_t* page, lds_u8* slot, int 
   __builtin_amdgcn_global_load_lds((global_ptr)(page + 8192 + 4 * lane), (lds_ptr)(slot + 8192), 4, 0, kNt);
 }
 
+// -inf over 16-byte units [a, b) of out, 16 bytes per lane and store.
+__device__ __forceinline__ void write_share(float* out, int64_t a, int64_t b, int lane) {
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  const f32x4 ninf = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  f32x4* dst = reinterpret_cast<f32x4*>(out);
+  for (int64_t i = a + lane; i < b; i += 64) __builtin_nontemporal_store(ninf, dst + i);
+}
+
 __global__ __launch_bounds__(256) void dma_stream_kernel(const uint8_t* pool, const int32_t* ids, int32_t n,
-                                                         uint32_t* sink) {
+                                                         uint32_t* sink, float* out, int64_t out_units,
+                                                         int32_t order) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves * 2 * kPageBytes];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int gw = blockIdx.x * kWaves + wave, nw = gridDim.x * kWaves;
   lds_u8* slots = (lds_u8*)(lds + wave * 2 * kPageBytes);
+  const int64_t wa = out_units * gw / nw, wb = out_units * (gw + 1) / nw;
+  // order 0: the first half of the grid writes first; 1: every wave writes
+  // first; 2: every wave reads first; 3: each page read is followed by an
+  // equal part of the wave's writes.
+  const bool write_first = order == 1 || (order == 0 && 2 * blockIdx.x < gridDim.x);
+  if (out && order != 3 && write_first) write_share(out, wa, wb, lane);
+  const int32_t my_pages = n > gw ? (n - gw + nw - 1) / nw : 0;
   int t = 0;
   for (int32_t p = gw; p < n; p += nw, ++t) {
     if (t >= 2) __builtin_amdgcn_s_waitcnt(wait_vm(kOpsPerPage));  // the page two back has landed
     const int32_t id = page_id(ids, p);
     dma_page(pool + (int64_t)id * kPageBytes, slots + (t & 1) * kPageBytes, lane);
+    if (out && order == 3)
+      write_share(out, wa + (wb - wa) * t / my_pages, wa + (wb - wa) * (t + 1) / my_pages, lane);
   }
+  if (out && order == 3 && my_pages == 0) write_share(out, wa, wb, lane);
+  if (out && order != 3 && !write_first) write_share(out, wa, wb, lane);
   __builtin_amdgcn_s_waitcnt(wait_vm(0));
   __syncthreads();
   if (lane == 0) sink[gw] = lds[wave * 2 * kPageBytes + 8192];
@@ -108,7 +133,28 @@ extern "C" int idx_read_stream(const void* pool, const int32_t* ids, int32_t n, 
   if (registers)
     reg_stream_kernel<<<grid, block, 0, stream>>>(static_cast<const uint8_t*>(pool), ids, n, sink);
   else
-    dma_stream_kernel<<<grid, block, 0, stream>>>(static_cast<const uint8_t*>(pool), ids, n, sink);
+    dma_stream_kernel<<<grid, block, 0, stream>>>(static_cast<const uint8_t*>(pool), ids, n, sink, nullptr, 0, 0);
+  return (int)hipGetLastError();
+}
+
+// As idx_read_stream (LDS DMA), and also writes -inf over out[0, out_bytes)
+// (device, 16-byte aligned, out_bytes a multiple of 16), each wave an equal
+// share, in the given order (0: the grid's first half writes before reading,
+// the second half after -- the decode's order; 1: all write first; 2: all
+// read first; 3: writes spread over the page reads).  Returns 0, -1 for a bad
+// argument, or the HIP error of the launch.
+extern "C" int idx_read_write_stream(const void* pool, const int32_t* ids, int32_t n, float* out,
+                                     int64_t out_bytes, int32_t order, uint32_t* sink, hipStream_t stream) {
+  if (!pool || !ids || !sink || n < 0 || (reinterpret_cast<uintptr_t>(pool) & 15u) != 0u || out_bytes < 0 ||
+      (out_bytes % 16) != 0 || (out_bytes > 0 && (!out || (reinterpret_cast<uintptr_t>(out) & 15u) != 0u)) ||
+      order < 0 || order > 3)
+    return -1;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                               hipSuccess || cus <= 0)
+    return -1;
+  dma_stream_kernel<<<dim3(2 * cus), dim3(256), 0, stream>>>(static_cast<const uint8_t*>(pool), ids, n, sink,
+                                                             out_bytes > 0 ? out : nullptr, out_bytes / 16, order);
   return (int)hipGetLastError();
 }
 
