@@ -229,6 +229,29 @@ def test_invalid_page_ids_give_nan(lib, shared):
     check_full(lib, wl, label=f"bad ids shared={shared}")
 
 
+@pytest.mark.parametrize("kind,shared", [("fp8", False), ("fp8", True), ("bf16", False)])
+def test_pool_size_past_int32(lib, kind, shared):
+    """A declared pool of 2^31 + 7 pages (more than a 32-bit signed id can name):
+    every non-negative id is then in the pool, negative ids still give NaN.  The
+    table names only pages of the small pool actually allocated, so nothing past
+    it is read; the oracle sees the real pool size, under which the same ids are
+    valid and invalid."""
+    wl = W.random_workload(65, kind, rows=3, table_width=4, num_pages=12,
+                           seqlens=[256, 200, 150], shared_table=shared)
+    wl.page_table[1] = -5
+    if not shared:
+        wl.page_table[4 + 2] = -1
+    ref = oracle.paged_mqa_logits(wl)
+    dw = W.to_device(wl)
+    dw.wl = dataclasses.replace(wl, num_pages=2 ** 31 + 7)
+    W.run_library(dw, lib)
+    torch.cuda.synchronize()
+    got = dw.out.cpu().numpy()
+    m = mask_of(wl)
+    assert np.array_equal(np.isnan(got), np.isnan(ref)), "NaN pattern"
+    assert_parity(got, ref, m, label=f"pool 2^31+7 {kind} shared={shared}")
+
+
 def test_all_256_fp8_codes(lib):
     """Every e4m3fn code reaches the logits exactly: key code c at dim 0 of one
     position, q = e_0 for head 0, w = e_0, s = +1 -> ReLU(dec(c)); s = -1 -> ReLU(-dec(c))."""
