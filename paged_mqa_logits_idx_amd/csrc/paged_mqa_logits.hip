@@ -1238,15 +1238,27 @@ __global__ __launch_bounds__(64 * kStoreWaves) void store_keys_kernel(const uint
 // later digits scan the list instead of the row, and the segments' counts
 // above and at the final key come from those counts and the list, so the
 // compaction reads the row only once more.  A longer row is re-read from
-// memory by each pass.
+// memory by each pass.  A listed row that takes at most a quarter of its
+// keys (1024-thread kernel) skips that compaction sweep: the list sweep also
+// marks the positions above the first digit in an LDS bitmap, the listed keys
+// are marked there (above the final key) or in a second bitmap (at it), and
+// thread t writes the taken positions of bitmap word t after one scan over
+// the threads' (above, at) counts.
 constexpr int kTopkBins = 2048;
+
+// Bitmap compaction (sparse rows) in the 1024-thread kernel only: the rows of
+// the 256-thread kernel are at most 6,144 long, and there it measured slower
+// (4096-row prefill top-k 35.1 -> 35.9 us, with no sparse row to gain on).
+template <int THREADS>
+constexpr bool kTopkBitmap = THREADS >= 1024;
 
 template <int THREADS, int CAP, int CAND>
 struct TopkShared {
   static constexpr int kThreads = THREADS;
   uint32_t vals[CAP];    // the staged row's order keys, when it fits
   uint32_t cand[CAND];   // positions of the keys sharing the first digit
-  uint32_t hist[kTopkBins];
+  uint32_t hist[kTopkBins];  // (after the last digit: bitmap of the listed keys at the final key)
+  uint32_t above[kTopkBitmap<THREADS> ? CAP / 32 : 1];  // bitmap of the positions whose key is above the final key
   uint32_t wave_gt[THREADS / 64], wave_eq[THREADS / 64];
   uint32_t pick[3];      // chosen digit, candidates in the digits above it, in it
   uint32_t ncand;
@@ -1467,6 +1479,9 @@ __device__ __forceinline__ void topk_row(TopkShared<THREADS, CAP, CAND>& sh, con
   const int32_t s0 = min(wave * seg, L), s1 = min(s0 + seg, L);
   // Radix select.  Invariant: 1 <= need <= candidates matching (prefix, mask).
   uint32_t prefix = 0u, mask = 0u, need = (uint32_t)k;
+  static_assert(CAP / 32 <= THREADS, "one bitmap word per thread");
+  if (kTopkBitmap<THREADS> && RES && 4 * (int64_t)k <= (int64_t)L && tid < CAP / 32)
+    sh.above[tid] = 0u;  // (a bitmap row's; ordered before the list sweep by radix_step's barriers)
   row_histogram<RES, THREADS, kSteps>(sh, x, L, 0, prefix, mask, vo != nullptr);
   uint32_t in_digit = radix_step(sh, 0, prefix, mask, need, wave, lane);
   bool counted = false;  // sh.wave_gt / wave_eq hold the segments' counts
@@ -1474,6 +1489,10 @@ __device__ __forceinline__ void topk_row(TopkShared<THREADS, CAP, CAND>& sh, con
     // RES rows whose first digit fits the list: one sweep over this wave's
     // segment counts the keys above the digit and lists the positions in it.
     const bool listed = RES && in_digit <= (uint32_t)CAND;
+    // Rows that take at most a quarter of their keys are compacted from
+    // bitmaps of the taken positions (below); denser rows by the sweep over
+    // the segments further down, whose cost does not grow with the count.
+    const bool bitmap = kTopkBitmap<THREADS> && listed && 4 * (int64_t)k <= (int64_t)L;
     if (listed) {
       static_assert(4 * kSteps <= 32, "a lane's digit bits fill one word");
       uint32_t lane_g = 0u, eqb = 0u;  // bit 4j+e: position s0 + 256j + 4*lane + e has the digit
@@ -1481,13 +1500,17 @@ __device__ __forceinline__ void topk_row(TopkShared<THREADS, CAP, CAND>& sh, con
       for (int32_t c0 = s0; c0 < s1; c0 += 256, ++j) {  // (at most kSteps steps: seg <= 256 * kSteps)
         uint32_t kk[4];
         keys4<true>(sh, x, c0 + 4 * lane, s1, kk);
+        uint32_t gb = 0u;  // bit e: position c0 + 4*lane + e is above the digit
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const bool ok = c0 + 4 * lane + e < s1;
           const uint32_t key = kk[e] & mask;
-          lane_g += (ok && key > prefix) ? 1u : 0u;
+          gb |= (ok && key > prefix ? 1u : 0u) << e;
           eqb |= (ok && key == prefix ? 1u : 0u) << (4 * j + e);
         }
+        lane_g += __builtin_popcount(gb);
+        // (c0 is a multiple of 256: the lane's 4 positions lie in one bitmap word)
+        if (bitmap && gb != 0u) atomicOr(&sh.above[(c0 + 4 * lane) >> 5], gb << ((4 * lane) & 31));
       }
       {
         const uint32_t m = __builtin_popcount(eqb);
@@ -1522,7 +1545,7 @@ __device__ __forceinline__ void topk_row(TopkShared<THREADS, CAP, CAND>& sh, con
       const uint32_t in_d = radix_step(sh, pass, prefix, mask, need, wave, lane);
       if (need == in_d) break;  // the whole digit is taken: no finer digit needed
     }
-    if (listed) {
+    if (listed && !bitmap) {
       // Keys outside the first digit are above the final key exactly when
       // they are above the digit (counted); the listed ones are counted here
       // into the segment that holds them.
@@ -1535,6 +1558,53 @@ __device__ __forceinline__ void topk_row(TopkShared<THREADS, CAP, CAND>& sh, con
       }
       __syncthreads();
       counted = true;
+    }
+    if (bitmap) {
+      // Keys outside the first digit are above the final key exactly when
+      // they are above the digit (marked by the list sweep); the listed keys
+      // above the final key join that bitmap, those at it go to a second one
+      // (the histogram, clear after the last pick).
+      uint32_t* at_key = sh.hist;
+      for (int32_t i = tid; i < (int32_t)in_digit; i += THREADS) {
+        const uint32_t pos = sh.cand[i];
+        const uint32_t key = sh.vals[pos] & mask;
+        if (key > prefix) atomicOr(&sh.above[pos >> 5], 1u << (pos & 31));
+        else if (key == prefix) atomicOr(&at_key[pos >> 5], 1u << (pos & 31));
+      }
+      __syncthreads();
+      // Compaction from the bitmaps: thread t owns positions 32t .. 32t+31; one
+      // scan over the threads of (keys above, keys at) gives each its first
+      // slot, and it writes its taken positions in order.
+      const int32_t words = (L + 31) >> 5;
+      const uint32_t ab = tid < words ? sh.above[tid] : 0u, eb = tid < words ? at_key[tid] : 0u;
+      const uint32_t c = (uint32_t)__builtin_popcount(ab) | ((uint32_t)__builtin_popcount(eb) << 16);
+      const uint32_t incl = wave_inclusive_scan_u32(c, lane);  // (each half stays below 2^16)
+      if (lane == 63) sh.wave_gt[wave] = incl;
+      __syncthreads();
+      uint32_t ex = incl - c;
+      for (int w = 0; w < wave; ++w) ex += sh.wave_gt[w];
+      auto emit_bits = [&](auto plain) {
+        uint32_t gl = ex & 0xFFFFu, ql = ex >> 16;
+        uint32_t bits = ab | eb;
+        while (bits != 0u) {
+          const int b = __builtin_ctz(bits);
+          const bool gt = (ab >> b) & 1u;
+          if (gt || ql < need) {
+            const uint32_t slot = gl + min(ql, need);
+            const int32_t pos = 32 * tid + b;
+            io[slot] = pos;
+            if (vo) vo[slot] = key_value<decltype(plain)::value>(sh.vals[pos], x, pos);
+          }
+          gl += gt ? 1u : 0u;
+          ql += gt ? 0u : 1u;
+          bits &= bits - 1u;
+        }
+      };
+      if (sh.special == 0u) emit_bits(std::true_type{});
+      else emit_bits(std::false_type{});
+      for (int i = tid; i < kTopkBins; i += THREADS) at_key[i] = 0u;  // the next row's first histogram
+      __syncthreads();  // wave_gt / vals / cand / hist are rewritten by the next row
+      return;
     }
   }
 

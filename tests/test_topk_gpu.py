@@ -89,6 +89,7 @@ def check_selection(lib, vals, seqlens, k, row_stride=None):
     (5, 6144, 700, "equal"), (6, 20000, 2048, "sample_low"), (6, 20000, 2048, "sample_high"),
     (6, 5000, 2048, "sample_low"), (6, 5000, 300, "sample_high"),
     (6, 3000, 2000, "zeros"), (6, 9000, 7000, "zeros"),
+    (6, 9000, 300, "zeros"), (6, 20000, 700, "ties"),  # sparse rows: compaction from bitmaps
     (8, 36000, 3000, "special"),  # NaN, +-0, +-inf in rows longer than the LDS stage
     (300, 6200, 64, "normal"),   # more rows than one-per-CU workgroups: taken last first
     (1100, 700, 200, "ties")])   # more rows than four-per-CU workgroups: taken last first
