@@ -1254,17 +1254,14 @@ __global__ __launch_bounds__(64 * kStoreWaves) void store_keys_kernel(const uint
 // later digits scan the list instead of the row, and the segments' counts
 // above and at the final key come from those counts and the list, so the
 // compaction reads the row only once more.  A longer row is re-read from
-// memory by each pass.  A listed row that takes at most a quarter of its
-// keys (1024-thread kernel) skips that compaction sweep: the list sweep also
-// marks the positions above the first digit in an LDS bitmap, the listed keys
-// are marked there (above the final key) or in a second bitmap (at it), and
-// thread t writes the taken positions of bitmap word t after one scan over
-// the threads' (above, at) counts.
+// memory by each pass.  A staged row that takes at most a quarter of its
+// keys (1024-thread kernel) goes another way after the first digit: each
+// thread keeps bit words of its own 32 positions (topk_row_owned).
 constexpr int kTopkBins = 2048;
 
-// Bitmap compaction (sparse rows) in the 1024-thread kernel only: the rows of
-// the 256-thread kernel are at most 6,144 long, and there it measured slower
-// (4096-row prefill top-k 35.1 -> 35.9 us, with no sparse row to gain on).
+// Per-thread bit words (sparse rows) in the 1024-thread kernel only: the rows
+// of the 256-thread kernel are at most 6,144 long, and bitmap compaction
+// measured slower there (4096-row prefill top-k 35.1 -> 35.9 us).
 template <int THREADS>
 constexpr bool kTopkBitmap = THREADS >= 1024;
 
@@ -1273,8 +1270,7 @@ struct TopkShared {
   static constexpr int kThreads = THREADS;
   uint32_t vals[CAP];    // the staged row's order keys, when it fits
   uint32_t cand[CAND];   // positions of the keys sharing the first digit
-  uint32_t hist[kTopkBins];  // (after the last digit: bitmap of the listed keys at the final key)
-  uint32_t above[kTopkBitmap<THREADS> ? CAP / 32 : 1];  // bitmap of the positions whose key is above the final key
+  uint32_t hist[kTopkBins];
   uint32_t wave_gt[THREADS / 64], wave_eq[THREADS / 64];
   uint32_t pick[3];      // chosen digit, candidates in the digits above it, in it
   uint32_t ncand;
@@ -1482,6 +1478,87 @@ __device__ __forceinline__ void row_histogram(SH& sh, const float* x, int32_t L,
   }
 }
 
+// Rows of the 1024-thread kernel that take at most a quarter of their keys,
+// from the first digit on.  Thread t owns the 32 positions 32t .. 32t+31 and
+// keeps them as two words of bits: `ab`, its keys above the current digit,
+// and `eb`, its keys in it.  The later digits count only the positions in eb
+// (their keys re-read from the stage), the final key splits eb into keys above
+// it and keys at it, and one block scan of the packed counts gives each
+// thread its first output slot.  No position list and no shared bitmaps.
+template <int THREADS, int CAP, int CAND>
+__device__ __forceinline__ void topk_row_owned(TopkShared<THREADS, CAP, CAND>& sh, const float* x, int32_t L,
+                                               int32_t* io, float* vo, uint32_t prefix, uint32_t mask,
+                                               uint32_t need, uint32_t in_digit, int wave, int lane) {
+  static_assert(CAP == 32 * THREADS, "one 32-position word per thread");
+  const int32_t p0 = 32 * (int32_t)threadIdx.x;
+  uint32_t ab = 0u, eb = 0u;
+  if (p0 < L) {
+    // After the first digit, mask keeps its 11 bits: a key is in the digit
+    // when it is >= prefix and below the next digit's first key.
+    const uint32_t next = prefix + (1u << topk_shift(0));  // 0 for the top digit
+    uint32_t ge = 0u, gt = 0u;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      // lane l starts at chunk l % 8: the 8 lanes that one 16-byte LDS read
+      // serves at a time then cover distinct banks
+      const int ch = (c + lane) & 7;
+      const u32x4 kk = *reinterpret_cast<const u32x4*>(&sh.vals[p0 + 4 * ch]);
+      uint32_t g4 = 0u, t4 = 0u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        g4 |= (kk[e] >= prefix ? 1u : 0u) << e;
+        t4 |= (kk[e] >= next ? 1u : 0u) << e;
+      }
+      ge |= g4 << (4 * ch);
+      gt |= t4 << (4 * ch);
+    }
+    if (next == 0u) gt = 0u;
+    const uint32_t valid = (L - p0 >= 32) ? ~0u : ((1u << (L - p0)) - 1u);
+    ab = gt & valid;
+    eb = ge & ~gt & valid;
+  }
+  for (int pass = 1; pass < 3 && need != in_digit; ++pass) {
+    const int shift = topk_shift(pass);
+    const uint32_t dmask = topk_dmask(pass);
+    for (uint32_t bits = eb; bits != 0u; bits &= bits - 1u) {
+      const uint32_t key = sh.vals[p0 + __builtin_ctz(bits)];
+      if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & dmask], 1u);
+    }
+    in_digit = radix_step(sh, pass, prefix, mask, need, wave, lane);
+  }
+  uint32_t at = 0u;  // keys at the final key (all of them taken when need == in_digit)
+  for (uint32_t bits = eb; bits != 0u; bits &= bits - 1u) {
+    const int b = __builtin_ctz(bits);
+    const uint32_t key = sh.vals[p0 + b] & mask;
+    if (key > prefix) ab |= 1u << b;
+    else if (key == prefix) at |= 1u << b;
+  }
+  const uint32_t c = (uint32_t)__builtin_popcount(ab) | ((uint32_t)__builtin_popcount(at) << 16);
+  const uint32_t incl = wave_inclusive_scan_u32(c, lane);  // (each half stays below 2^16)
+  if (lane == 63) sh.wave_gt[wave] = incl;
+  __syncthreads();
+  uint32_t ex = incl - c;
+  for (int w = 0; w < wave; ++w) ex += sh.wave_gt[w];
+  // a key at the final key is taken while fewer than `need` came before it
+  auto emit_bits = [&](auto plain) {
+    uint32_t gl = ex & 0xFFFFu, ql = ex >> 16;
+    for (uint32_t bits = ab | at; bits != 0u; bits &= bits - 1u) {
+      const int b = __builtin_ctz(bits);
+      const bool above = (ab >> b) & 1u;
+      if (above || ql < need) {
+        const uint32_t slot = gl + min(ql, need);
+        io[slot] = p0 + b;
+        if (vo) vo[slot] = key_value<decltype(plain)::value>(sh.vals[p0 + b], x, p0 + b);
+      }
+      gl += above ? 1u : 0u;
+      ql += above ? 0u : 1u;
+    }
+  };
+  if (sh.special == 0u) emit_bits(std::true_type{});
+  else emit_bits(std::false_type{});
+  __syncthreads();  // wave_gt / vals are rewritten by the next row
+}
+
 // Row of L > k candidates.  RES: the row is in sh.vals (L <= CAP).
 template <bool RES, int THREADS, int CAP, int CAND>
 __device__ __forceinline__ void topk_row(TopkShared<THREADS, CAP, CAND>& sh, const float* x, int32_t L,
@@ -1495,20 +1572,19 @@ __device__ __forceinline__ void topk_row(TopkShared<THREADS, CAP, CAND>& sh, con
   const int32_t s0 = min(wave * seg, L), s1 = min(s0 + seg, L);
   // Radix select.  Invariant: 1 <= need <= candidates matching (prefix, mask).
   uint32_t prefix = 0u, mask = 0u, need = (uint32_t)k;
-  static_assert(CAP / 32 <= THREADS, "one bitmap word per thread");
-  if (kTopkBitmap<THREADS> && RES && 4 * (int64_t)k <= (int64_t)L && tid < CAP / 32)
-    sh.above[tid] = 0u;  // (a bitmap row's; ordered before the list sweep by radix_step's barriers)
   row_histogram<RES, THREADS, kSteps>(sh, x, L, 0, prefix, mask, vo != nullptr);
   uint32_t in_digit = radix_step(sh, 0, prefix, mask, need, wave, lane);
+  if constexpr (kTopkBitmap<THREADS> && RES) {
+    if (4 * (int64_t)k <= (int64_t)L) {  // sparse rows: compaction from per-thread bit words
+      topk_row_owned(sh, x, L, io, vo, prefix, mask, need, in_digit, wave, lane);
+      return;
+    }
+  }
   bool counted = false;  // sh.wave_gt / wave_eq hold the segments' counts
   if (need != in_digit) {
     // RES rows whose first digit fits the list: one sweep over this wave's
     // segment counts the keys above the digit and lists the positions in it.
     const bool listed = RES && in_digit <= (uint32_t)CAND;
-    // Rows that take at most a quarter of their keys are compacted from
-    // bitmaps of the taken positions (below); denser rows by the sweep over
-    // the segments further down, whose cost does not grow with the count.
-    const bool bitmap = kTopkBitmap<THREADS> && listed && 4 * (int64_t)k <= (int64_t)L;
     if (listed) {
       static_assert(4 * kSteps <= 32, "a lane's digit bits fill one word");
       uint32_t lane_g = 0u, eqb = 0u;  // bit 4j+e: position s0 + 256j + 4*lane + e has the digit
@@ -1525,8 +1601,6 @@ __device__ __forceinline__ void topk_row(TopkShared<THREADS, CAP, CAND>& sh, con
           eqb |= (ok && key == prefix ? 1u : 0u) << (4 * j + e);
         }
         lane_g += __builtin_popcount(gb);
-        // (c0 is a multiple of 256: the lane's 4 positions lie in one bitmap word)
-        if (bitmap && gb != 0u) atomicOr(&sh.above[(c0 + 4 * lane) >> 5], gb << ((4 * lane) & 31));
       }
       {
         const uint32_t m = __builtin_popcount(eqb);
@@ -1561,7 +1635,7 @@ __device__ __forceinline__ void topk_row(TopkShared<THREADS, CAP, CAND>& sh, con
       const uint32_t in_d = radix_step(sh, pass, prefix, mask, need, wave, lane);
       if (need == in_d) break;  // the whole digit is taken: no finer digit needed
     }
-    if (listed && !bitmap) {
+    if (listed) {
       // Keys outside the first digit are above the final key exactly when
       // they are above the digit (counted); the listed ones are counted here
       // into the segment that holds them.
@@ -1574,53 +1648,6 @@ __device__ __forceinline__ void topk_row(TopkShared<THREADS, CAP, CAND>& sh, con
       }
       __syncthreads();
       counted = true;
-    }
-    if (bitmap) {
-      // Keys outside the first digit are above the final key exactly when
-      // they are above the digit (marked by the list sweep); the listed keys
-      // above the final key join that bitmap, those at it go to a second one
-      // (the histogram, clear after the last pick).
-      uint32_t* at_key = sh.hist;
-      for (int32_t i = tid; i < (int32_t)in_digit; i += THREADS) {
-        const uint32_t pos = sh.cand[i];
-        const uint32_t key = sh.vals[pos] & mask;
-        if (key > prefix) atomicOr(&sh.above[pos >> 5], 1u << (pos & 31));
-        else if (key == prefix) atomicOr(&at_key[pos >> 5], 1u << (pos & 31));
-      }
-      __syncthreads();
-      // Compaction from the bitmaps: thread t owns positions 32t .. 32t+31; one
-      // scan over the threads of (keys above, keys at) gives each its first
-      // slot, and it writes its taken positions in order.
-      const int32_t words = (L + 31) >> 5;
-      const uint32_t ab = tid < words ? sh.above[tid] : 0u, eb = tid < words ? at_key[tid] : 0u;
-      const uint32_t c = (uint32_t)__builtin_popcount(ab) | ((uint32_t)__builtin_popcount(eb) << 16);
-      const uint32_t incl = wave_inclusive_scan_u32(c, lane);  // (each half stays below 2^16)
-      if (lane == 63) sh.wave_gt[wave] = incl;
-      __syncthreads();
-      uint32_t ex = incl - c;
-      for (int w = 0; w < wave; ++w) ex += sh.wave_gt[w];
-      auto emit_bits = [&](auto plain) {
-        uint32_t gl = ex & 0xFFFFu, ql = ex >> 16;
-        uint32_t bits = ab | eb;
-        while (bits != 0u) {
-          const int b = __builtin_ctz(bits);
-          const bool gt = (ab >> b) & 1u;
-          if (gt || ql < need) {
-            const uint32_t slot = gl + min(ql, need);
-            const int32_t pos = 32 * tid + b;
-            io[slot] = pos;
-            if (vo) vo[slot] = key_value<decltype(plain)::value>(sh.vals[pos], x, pos);
-          }
-          gl += gt ? 1u : 0u;
-          ql += gt ? 0u : 1u;
-          bits &= bits - 1u;
-        }
-      };
-      if (sh.special == 0u) emit_bits(std::true_type{});
-      else emit_bits(std::false_type{});
-      for (int i = tid; i < kTopkBins; i += THREADS) at_key[i] = 0u;  // the next row's first histogram
-      __syncthreads();  // wave_gt / vals / cand / hist are rewritten by the next row
-      return;
     }
   }
 
