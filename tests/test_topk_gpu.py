@@ -89,7 +89,7 @@ def check_selection(lib, vals, seqlens, k, row_stride=None):
     (5, 6144, 700, "equal"), (6, 20000, 2048, "sample_low"), (6, 20000, 2048, "sample_high"),
     (6, 5000, 2048, "sample_low"), (6, 5000, 300, "sample_high"),
     (6, 3000, 2000, "zeros"), (6, 9000, 7000, "zeros"),
-    (6, 9000, 300, "zeros"), (6, 20000, 700, "ties"),  # sparse rows: compaction from bitmaps
+    (6, 9000, 300, "zeros"), (6, 20000, 700, "ties"),  # sparse rows: per-thread bit words
     (8, 36000, 3000, "special"),  # NaN, +-0, +-inf in rows longer than the LDS stage
     (300, 6200, 64, "normal"),   # more rows than one-per-CU workgroups: taken last first
     (1100, 700, 200, "ties")])   # more rows than four-per-CU workgroups: taken last first
@@ -97,6 +97,20 @@ def test_topk_bit_exact(lib, rows, ncols, k, kind):
     rng = np.random.default_rng(rows * 7 + ncols + k)
     vals = values_of(rng, kind, rows, ncols)
     check_selection(lib, vals, lengths_for(rng, rows, ncols, k), k)
+
+
+@pytest.mark.parametrize("k", [1, 2048])
+@pytest.mark.parametrize("kind", ["normal", "special", "equal"])
+def test_topk_sparse_row_boundaries(lib, k, kind):
+    """The 1024-thread kernel finishes a staged row that takes at most a
+    quarter of its keys from per-thread 32-position bit words: lengths just
+    below, at and above 4k, a partial last word, and the full 32,768-key
+    stage (every word whole)."""
+    rng = np.random.default_rng(k * 3 + len(kind))
+    ncols = 32768
+    lens = [4 * k - 1, 4 * k, 4 * k + 1, 4 * k + 33, 32767, 32768, 20000 + 17]
+    vals = values_of(rng, kind, len(lens), ncols)
+    check_selection(lib, vals, np.array(lens, dtype=np.int32), k)
 
 
 def test_topk_reads_only_live_positions(lib):
