@@ -249,6 +249,21 @@ def test_fused_topk_prefill_full_size(lib):
     check_fused(lib, wl, 2048, ref_rows=[0, 1500, 2047, 2048, 4095])
 
 
+def test_fused_topk_fp8_prefill_full_size(lib):
+    """The 4096-token prefill with e4m3 keys: whole-table units of 88 pages,
+    so each wave's logits buffer flushes inside the unit, with the fused
+    call's ordinary stores."""
+    wl = W.config("4f")
+    check_fused(lib, wl, 2048, ref_rows=[3, 2049, 4095])
+
+
+def test_fused_topk_bf16_decode(lib):
+    """The 128-page bf16-key decode batch (64 rows), k = 2048: the bf16 decode
+    path with the fill off."""
+    wl = W.config("2b")
+    check_fused(lib, wl, 2048, ref_rows=[0, 31, 63])
+
+
 def test_fused_topk_graph_replay(lib):
     """Captured fused call: every replay gives the eager result."""
     wl = W.random_workload(46, "fp8", rows=16, table_width=64, num_pages=300)
